@@ -1,0 +1,324 @@
+/*
+ * pkb.h -- C ABI of libpkb.so: scaled-dot-product attention over a paged KV
+ * cache on AMD Instinct MI355X (gfx950).
+ *
+ * Operations (each defined by a FlashInfer documentation page):
+ *   - block-sparse attention with a paged KV cache
+ *     (page "flashinfer.attention.prims_ts.block_sparse_attention_with_paged_kv_cache",
+ *      signature and Parameters)                         -> bsa_plan / bsa_validate / bsa_run
+ *   - packed-Q paged prefill
+ *     (page "flashinfer.attention.prims_ts.batch_prefill_with_paged_kv_cache")
+ *                                                        -> paged_prefill_validate / _plan / _run
+ *   - single-token paged decode with caller scratch
+ *     (page "flashinfer.attention.prims_ts.prims_ts_batch_decode_with_kv_cache")
+ *                                                        -> paged_decode_validate / _workspace_size / _run
+ *   - prequantized Sage-style block-sparse attention
+ *     (page "flashinfer.cute_dsl.sparse.bsa_attn_sm120.bsa_attn_sm120_blk64_sage_fwd")
+ *                                                        -> bsa_sage_validate / bsa_sage_run
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership: every tensor, output, LSE buffer, work list and workspace is
+ *   caller-owned device memory (host memory where a parameter name ends in _h).
+ *   The library never allocates or frees device memory.  Plan structs are POD
+ *   values owned by the caller; there is nothing to destroy.
+ * Errors: every function returns an int status: PKB_OK (0) or a negative
+ *   pkb_status code.  Nothing is thrown and nothing aborts.  *_run functions
+ *   check static arguments and return before launching anything when they are
+ *   wrong.  pkb_status_string() describes a code.
+ * Synchronisation: *_run functions only enqueue work on the given HIP stream
+ *   (hipStream_t passed as void*; NULL = the default stream).  They never copy
+ *   device data to the host and never synchronise, so they may be captured in a
+ *   HIP graph.  *_validate and paged_prefill_plan read HOST copies of metadata
+ *   synchronously.
+ * Trust: *_run trusts live metadata (page IDs, offsets, lengths) exactly as the
+ *   pages state: callers that cannot guarantee it call *_validate first.
+ * Layouts: all tensors are contiguous unless a stride argument says otherwise;
+ *   strides are in ELEMENTS.  K/V page pools are HND: [P, Hkv, page_size, D].  A
+ *   combined cache [P, 2, Hkv, page_size, D] is passed as k = base,
+ *   v = base + Hkv*page_size*D with kv_page_stride = 2*Hkv*page_size*D.
+ * Numerics: bf16 inputs, fp32 accumulation, online softmax in base 2, output
+ *   rounded to bf16 (round-to-nearest-even) or written as fp32.  LSE is the
+ *   natural-log softmax normaliser in fp32, laid out [tokens, Hq]; a query row
+ *   with no admitted key gets an exact zero output and LSE = -inf.
+ * Memory contract for K/V: every live token (position < seq_len) must hold
+ *   finite values; slots at or past the live length and unreferenced pages are
+ *   never read into the result and may hold anything (NaN included).
+ */
+#ifndef PKB_H_
+#define PKB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKB_ABI_VERSION 1
+
+/* Largest max_seq_len accepted: 2^31 - 128, so that a 128-token padded tile end
+ * still fits in int32 (page "prims_ts_batch_decode_with_kv_cache", description of
+ * max_seq_len). */
+#define PKB_MAX_SEQ_LEN 2147483520
+
+enum pkb_status {
+  PKB_OK = 0,
+  PKB_ERR_ARG = -1,         /* a static argument is out of range / inconsistent */
+  PKB_ERR_SHAPE = -2,       /* a size or stride does not match the others */
+  PKB_ERR_DTYPE = -3,       /* unsupported dtype or dtype combination */
+  PKB_ERR_UNSUPPORTED = -4, /* valid request this library does not implement */
+  PKB_ERR_METADATA = -5,    /* live metadata violates its contract (validate) */
+  PKB_ERR_WORKSPACE = -6,   /* workspace / work list too small or missing */
+  PKB_ERR_HIP = -7          /* a HIP runtime call or launch failed */
+};
+
+enum pkb_dtype { PKB_BF16 = 0, PKB_FP32 = 1, PKB_I8 = 2, PKB_FP8E4M3 = 3 };
+enum pkb_mask { PKB_MASK_DENSE = 0, PKB_MASK_CAUSAL = 1 };
+
+/* Which metadata array a validate failure refers to. */
+enum pkb_field {
+  PKB_FIELD_NONE = 0,
+  PKB_FIELD_KV_INDPTR = 1,
+  PKB_FIELD_KV_INDICES = 2,
+  PKB_FIELD_SEQ_LENS = 3,
+  PKB_FIELD_BLOCK_INDPTR = 4,
+  PKB_FIELD_BLOCK_INDICES = 5,
+  PKB_FIELD_QO_INDPTR = 6,
+  PKB_FIELD_BLOCK_TABLES = 7,
+  PKB_FIELD_Q2K_INDEX = 8,
+  PKB_FIELD_Q2K_NUMS = 9,
+  PKB_FIELD_BLOCK_SIZES = 10
+};
+
+/* First contract violation found by a *_validate call: the array and the flat
+ * element index inside it (-1 when the failure is not tied to one element). */
+typedef struct {
+  int32_t field;
+  int64_t index;
+} pkb_bad_t;
+
+const char* pkb_status_string(int status);
+int pkb_abi_version(void);
+
+/* ======================================================================== */
+/* Block-sparse attention with a paged KV cache                              */
+/* (page "block_sparse_attention_with_paged_kv_cache": signature, Parameters) */
+/* ======================================================================== */
+
+/* Static (capacity-only) arguments.  The page plans from static capacities and
+ * binds live metadata only at run time.
+ *   B, Sq, Hq, Hkv, D      q is [B, Sq, Hq, D]; Hq % Hkv == 0; D in {128, 256}.
+ *   num_pages, page_size   K/V pools [num_pages, Hkv, page_size, D];
+ *                          page_size a positive multiple of 8.
+ *   q_block_size           query tokens per BSR row; (q_block_size*Hq/Hkv) % 8 == 0.
+ *   kv_block_size          KV tokens per logical block: 8, 16, 32 or a multiple of 64.
+ *   max_seq_len_kv         static maximum live KV length, 1..PKB_MAX_SEQ_LEN.
+ *   mask_type              PKB_MASK_DENSE or PKB_MASK_CAUSAL, applied per token
+ *                          inside the selected blocks; causal aligns query i to
+ *                          KV position seq_len - Sq + i.
+ *   window_left            -1 (off) or w >= 0: admits keys p-w..p; needs causal.
+ *   qkv_dtype, out_dtype   PKB_BF16 / (PKB_BF16 or PKB_FP32).
+ *   num_cus                compute units of the target device (for the grid).  */
+typedef struct {
+  int32_t B, Sq, Hq, Hkv, D;
+  int32_t num_pages, page_size;
+  int32_t q_block_size, kv_block_size;
+  int32_t max_seq_len_kv;
+  int32_t mask_type, window_left;
+  int32_t qkv_dtype, out_dtype;
+  int32_t num_cus;
+} bsa_static_args;
+
+/* Plan: derived launch geometry.  POD; copy freely. */
+typedef struct {
+  bsa_static_args a;
+  int32_t group;            /* Hq / Hkv */
+  int32_t rows_per_brow;    /* q_block_size * group: packed rows of one BSR row */
+  int32_t num_q_blocks;     /* ceil(Sq / q_block_size) */
+  int32_t num_kv_blocks;    /* ceil(max_seq_len_kv / kv_block_size) */
+  int32_t valid_words;      /* ceil(max_seq_len_kv / 32): row stride of kv_valid_bits */
+  int32_t waves;            /* wavefronts per workgroup (32 packed rows each) */
+  int32_t tile_m;           /* packed query rows per workgroup = 32 * waves */
+  int32_t tiles_per_brow;   /* ceil(rows_per_brow / tile_m) */
+  int32_t grid_x, grid_y, grid_z;
+  int32_t kernel_id;
+} bsa_plan_t;
+
+/* Checks the static arguments and fills *plan.  Host only, no device access. */
+int bsa_plan(const bsa_static_args* args, bsa_plan_t* plan);
+
+/* Host validation of live metadata (the page validates synchronously before the
+ * trusted run).  All pointers are HOST copies:
+ *   paged_kv_indptr_h [B+1]: starts at 0, strictly increasing, ends at n_indices.
+ *   paged_kv_indices_h [n_indices]: the first ceil(seq_len/page_size) IDs of every
+ *       request are in [0, num_pages) and there are enough of them.
+ *   block_indptr_h [B, Hkv, num_q_blocks+1]: absolute offsets into block_indices,
+ *       non-decreasing along each (b, kv head), every value in [0, n_block_indices].
+ *   block_indices_h: logical KV block IDs in [0, num_kv_blocks), distinct per row.
+ *   seq_lens_kv_h [B]: 0 <= seq_len <= max_seq_len_kv.
+ * Returns PKB_OK or PKB_ERR_METADATA with *bad set to the first violation in the
+ * order: kv_indptr, seq_lens, then per request the CSR sufficiency (reported on
+ * kv_indptr[b+1]) and its live IDs, then block_indptr, then block_indices row by
+ * row (each in increasing flat index).  bad may be NULL. */
+int bsa_validate(const bsa_plan_t* plan,
+                 const int32_t* paged_kv_indptr_h, const int32_t* paged_kv_indices_h,
+                 int64_t n_indices,
+                 const int32_t* block_indptr_h, const int32_t* block_indices_h,
+                 int64_t n_block_indices,
+                 const int32_t* seq_lens_kv_h, pkb_bad_t* bad);
+
+/* Trusted run.  Device pointers:
+ *   q [B, Sq, Hq, D] bf16;  k, v page pools (strides in elements: one page is
+ *   kv_page_stride apart, one KV head kv_head_stride apart, tokens D apart);
+ *   paged_kv_indptr/indices, block_indptr/indices, seq_lens_kv as in bsa_validate;
+ *   kv_valid_bits [B, valid_words] uint32 or NULL (bit t%32 of word t/32, LSB
+ *   first; 0 excludes token t);  sm_scale <= 0 selects 1/sqrt(D);
+ *   out [B, Sq, Hq, D] in plan->a.out_dtype;  lse [B*Sq, Hq] fp32 or NULL.
+ * No workspace is needed. */
+int bsa_run(const bsa_plan_t* plan, const void* q, const void* k, const void* v,
+            int64_t kv_page_stride, int64_t kv_head_stride,
+            const int32_t* paged_kv_indptr, const int32_t* paged_kv_indices,
+            const int32_t* block_indptr, const int32_t* block_indices,
+            const int32_t* seq_lens_kv, const uint32_t* kv_valid_bits, float sm_scale,
+            void* out, float* lse, void* stream);
+
+/* ======================================================================== */
+/* Packed-Q paged prefill                                                     */
+/* (page "batch_prefill_with_paged_kv_cache": description, Parameters)        */
+/* ======================================================================== */
+
+/*   B, Hq, Hkv, D   q/out are [total_q, Hq, D]; D in {128, 256}.
+ *   num_pages, page_size  HND pools; page_size in {16, 32, 64, 128}.
+ *   block_table_width     C: block_tables is [B, C] with row stride >= C.
+ *   mask_type, window_left as for bsa; causal aligns query i of request b to
+ *                         position seq_len[b] - qlen[b] + i.                */
+typedef struct {
+  int32_t B, Hq, Hkv, D;
+  int32_t num_pages, page_size;
+  int32_t total_q;
+  int32_t block_table_width;
+  int32_t mask_type, window_left;
+  int32_t qkv_dtype, out_dtype;
+  int32_t num_cus;
+} prefill_static_args;
+
+typedef struct {
+  prefill_static_args a;
+  int32_t group;
+  int32_t waves, tile_m;
+  int32_t n_work;           /* work items (= grid_x); each is (b, first packed row) */
+  int32_t grid_x, grid_y;
+  int32_t kernel_id;
+  int64_t kv_tokens;        /* sum over work items of visited KV positions */
+} pkb_prefill_plan_t;
+
+/* Host validation of prefill metadata (host copies):
+ *   qo_indptr_h [B+1]: starts at 0, strictly increasing, ends at total_q.
+ *   seq_lens_kv_h [B]: >= 0; causal additionally needs qlen[b] <= seq_len[b].
+ *   block_tables_h [B, row_stride]: ceil(seq_len/page_size) <= C (else the
+ *       failure is reported on seq_lens[b]) and those leading entries are in
+ *       [0, num_pages).
+ * Order: qo_indptr, seq_lens, block_tables. */
+int paged_prefill_validate(const prefill_static_args* args, const int32_t* qo_indptr_h,
+                           const int32_t* seq_lens_kv_h, const int32_t* block_tables_h,
+                           int64_t block_table_row_stride, pkb_bad_t* bad);
+
+/* Reads host qo_indptr / seq_lens to build the work list (the page derives exact
+ * plan bounds from host request metadata).  worklist_h receives 2*n_work int32:
+ * (request, first packed query row of the tile within the request), sorted by
+ * decreasing visited-KV span, ties by (request, row).  Returns PKB_ERR_WORKSPACE
+ * (with *n_work set) when worklist_cap < n_work; worklist_h may then be NULL. */
+int paged_prefill_plan(const prefill_static_args* args, const int32_t* qo_indptr_h,
+                       const int32_t* seq_lens_kv_h, pkb_prefill_plan_t* plan,
+                       int32_t* worklist_h, int64_t worklist_cap, int64_t* n_work);
+
+/* Trusted run.  worklist_d: device copy of the plan's work list.  output_scale
+ * multiplies the normalised output; out dtype from the plan. */
+int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
+                      const void* q, const void* k_cache, const void* v_cache,
+                      int64_t kv_page_stride, int64_t kv_head_stride,
+                      const int32_t* qo_indptr, const int32_t* block_tables,
+                      int64_t block_table_row_stride, const int32_t* seq_lens_kv,
+                      float sm_scale, float output_scale, void* out, float* lse,
+                      void* stream);
+
+/* ======================================================================== */
+/* Single-token paged decode, split-KV with a merge pass                      */
+/* (page "prims_ts_batch_decode_with_kv_cache": description, Parameters)      */
+/* ======================================================================== */
+
+/* Static policy from max_seq_len (the page selects its policy from the static
+ * maximum): the number of KV splits per (request, KV head), the split length
+ * in tokens, and the workspace bytes paged_decode_run needs.  The workspace
+ * needs no zeroing. */
+int paged_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t max_seq_len, int32_t page_size, int32_t num_cus,
+                                size_t* bytes, int32_t* num_splits, int32_t* split_len);
+
+/* Host validation (host copies): indptr starts at 0, strictly increasing, ends at
+ * n_indices; 1 <= seq_len <= max_seq_len; each request owns
+ * ceil(seq_len/page_size) CSR entries and those IDs are in [0, num_pages).
+ * Order: kv_indptr, seq_lens, then per request the CSR sufficiency (reported on
+ * kv_indptr[b+1]) and its live IDs. */
+int paged_decode_validate(int32_t B, int32_t num_pages, int32_t page_size,
+                          int32_t max_seq_len, const int32_t* paged_kv_indptr_h,
+                          const int32_t* paged_kv_indices_h, int64_t n_indices,
+                          const int32_t* seq_lens_h, pkb_bad_t* bad);
+
+/* Trusted run.  query [B, Hq, D] bf16; k/v pools as above; bmm1_scale is the
+ * softmax scale (<= 0 selects 1/sqrt(D)); bmm2_scale multiplies the output;
+ * out [B, Hq, D] (out_dtype), lse [B, Hq] fp32 or NULL; workspace of at least
+ * paged_decode_workspace_size() bytes, exclusive to this launch until it ends. */
+int paged_decode_run(const void* query, const void* k, const void* v,
+                     int64_t kv_page_stride, int64_t kv_head_stride,
+                     const int32_t* paged_kv_indptr, const int32_t* paged_kv_indices,
+                     const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                     int32_t D, int32_t num_pages, int32_t page_size, int32_t max_seq_len,
+                     int32_t mask_type, int32_t window_left, float bmm1_scale,
+                     float bmm2_scale, int32_t out_dtype, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, int32_t num_cus,
+                     void* stream);
+
+/* ======================================================================== */
+/* Sage-style prequantized block-sparse attention                            */
+/* (page "bsa_attn_sm120_blk64_sage_fwd": signature, Parameters, Notes)       */
+/* ======================================================================== */
+
+/* Host validation: block_sparse_num in [0, capacity]; q2k_block_nums (if given
+ * and not uniform) in [0, capacity]; the first n indices of every row in
+ * [0, ceil(Sk/64)) and distinct; block_sizes (if given) in [0, 64].
+ * Order: q2k_nums, q2k_index, block_sizes. */
+int bsa_sage_validate(const int32_t* q2k_block_index_h, int32_t capacity,
+                      int32_t block_sparse_num, const int32_t* block_sizes_h,
+                      int32_t block_sizes_rank, const int32_t* q2k_block_nums_h,
+                      int32_t uniform_block_count, int32_t B, int32_t H, int32_t Sq,
+                      int32_t Sk, pkb_bad_t* bad);
+
+/* Trusted run (MHA, D = 128, 64-token blocks, no mask inside blocks, no LSE).
+ *   q [B,H,Sq,128] int8, k [B,H,Sk,128] int8,
+ *   v_fp8 [B,H,128,ceil(Sk/64)*64] OCP E4M3FN in HDS layout (tokens contiguous),
+ *   q_scale [B,H,ceil(Sq/128)*4] (one per 32 rows), k_scale [B,H,ceil(Sk/64)],
+ *   v_scale [B,H,128] fp32;
+ *   q2k_block_index [B,H,ceil(Sq/64),capacity] int32;
+ *   q2k_block_nums [B,H,ceil(Sq/64)] or NULL, used when non-NULL and
+ *   uniform_block_count == 0, else every row uses block_sparse_num;
+ *   block_sizes (NULL = 64) of rank 1 [nkb], 2 [B,nkb] or 3 [B,H,nkb]:
+ *   valid-token count of each KV block (its first tokens);
+ *   contiguous_block_indices: accepted, needs uniform_block_count, otherwise
+ *   ignored;  softmax_scale <= 0 selects 1/sqrt(128);
+ *   out [B,H,Sq,128] bf16.  A row selecting zero blocks is written as zeros. */
+int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
+                 const float* q_scale, const float* k_scale, const float* v_scale,
+                 const int32_t* q2k_block_index, int32_t capacity,
+                 int32_t block_sparse_num, const int32_t* block_sizes,
+                 int32_t block_sizes_rank, const int32_t* q2k_block_nums,
+                 int32_t uniform_block_count, int32_t contiguous_block_indices,
+                 int32_t B, int32_t H, int32_t Sq, int32_t Sk, float softmax_scale,
+                 void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKB_H_ */
