@@ -100,6 +100,9 @@ typedef struct {
 
 const char* pkb_status_string(int status);
 int pkb_abi_version(void);
+/* Text of the last HIP runtime error seen by a *_run call on this thread (the
+ * detail behind PKB_ERR_HIP). */
+const char* pkb_last_hip_error(void);
 
 /* ======================================================================== */
 /* Block-sparse attention with a paged KV cache                              */

@@ -1,0 +1,73 @@
+// pkb_internal.h -- kernel parameter blocks and launcher declarations shared by
+// the host API (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkb {
+
+enum AttnMode { kModeBsa = 0, kModePrefill = 1, kModeDecode = 2 };
+
+// Keys per KV tile of the bf16 attention kernel (one LDS tile = 8 chunks of 8).
+constexpr int kKvTile = 64;
+
+// Everything the bf16 attention kernel needs, passed by value.
+struct AttnParams {
+  const uint16_t* q;          // bf16 bits; token-major [tokens, Hq, D]
+  const uint16_t* k;          // page pools (element strides below)
+  const uint16_t* v;
+  void* out;                  // [tokens, Hq, D] bf16 or fp32
+  float* lse;                 // [tokens, Hq] or null
+  float* part;                // decode split partials [B, Hq, S, D+2] or null
+  const int32_t* kv_indptr;   // CSR page IDs (bsa, decode)
+  const int32_t* kv_indices;
+  const int32_t* block_tables;  // row-strided table (prefill)
+  const int32_t* seq_lens;
+  const int32_t* qo_indptr;     // prefill
+  const int32_t* block_indptr;  // bsa [B, Hkv, nqb+1]
+  const int32_t* block_indices;
+  const uint32_t* valid_bits;   // bsa [B, valid_words] or null
+  const int32_t* worklist;      // prefill (request, first row) pairs
+  int64_t kv_page_stride, kv_head_stride, bt_stride;
+  int B, Sq, Hq, Hkv, G, page_size;
+  int qbs, kvbs, nqb, tiles_per_brow, rows_per_brow, valid_words;
+  int causal, window_left;
+  int num_splits, split_len;
+  int out_f32;
+  float scale_log2;   // softmax scale * log2(e)
+  float out_scale;
+};
+
+struct MergeParams {
+  const float* part;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  int B, Hq, num_splits, split_len, out_f32;
+  float out_scale;
+};
+
+struct SageParams {
+  const int8_t* q;
+  const int8_t* k;
+  const uint8_t* v;           // e4m3 HDS [B, H, 128, Skp]
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* index;
+  const int32_t* nums;        // null => block_sparse_num
+  const int32_t* block_sizes; // null => 64
+  uint16_t* out;
+  int B, H, Sq, Sk, Skp, nqb, nkb, capacity, block_sparse_num;
+  int bs_rank, qs_len;
+  float scale_log2;
+};
+
+size_t attn_lds_bytes(int D);
+hipError_t launch_attn(const AttnParams& p, int D, int waves, int mode, dim3 grid,
+                       hipStream_t stream);
+hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream);
+hipError_t launch_sage(const SageParams& p, hipStream_t stream);
+
+}  // namespace pkb

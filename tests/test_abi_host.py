@@ -1,0 +1,335 @@
+"""CPU tests of the C ABI: exports, static checks, plans and host validation.
+
+No kernel runs here.  Plan fields, validation status + first bad index, the
+prefill work list and the decode split policy must match the Python statement
+of the same rules (oracle/metadata.py) bit for bit.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import paged_kv_block_amd as P
+from paged_kv_block_amd import _lib as C
+from gen import workloads as W
+from oracle import metadata as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "pkb.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 14
+    out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(names) == set(C.EXPORTS)
+    L = P.lib()
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_status_strings_and_version():
+    L = P.lib()
+    assert L.pkb_abi_version() == 1
+    for st in range(0, -8, -1):
+        assert L.pkb_status_string(st).decode() not in ("", "unknown status")
+    assert M.MAX_SEQ_LEN == 2147483520 == C.PKB_MAX_SEQ_LEN   # 2^31 - 128
+
+
+def _c_bsa_plan(args):
+    a = C.BsaStaticArgs(*[args[k] for k in (
+        "B", "Sq", "Hq", "Hkv", "D", "num_pages", "page_size", "q_block_size", "kv_block_size",
+        "max_seq_len_kv", "mask_type", "window_left", "qkv_dtype", "out_dtype", "num_cus")])
+    plan = C.BsaPlan()
+    st = P.lib().bsa_plan(ctypes.byref(a), ctypes.byref(plan))
+    return st, plan
+
+
+def _rand_static(rng):
+    """Mostly valid static arguments, each field occasionally out of contract."""
+    def pick(good, bad):
+        return int(rng.choice(bad)) if rng.random() < 0.06 else int(rng.choice(good))
+    Hkv = pick([1, 2, 8], [3])
+    return dict(B=pick([1, 2, 4], [0]), Sq=pick([1, 17, 64, 300], [0]),
+                Hq=Hkv * pick([1, 2, 4, 8], [1]) if rng.random() > 0.05 else 3,
+                Hkv=Hkv, D=pick([128, 256], [64]), num_pages=pick([1, 99], [0]),
+                page_size=pick([8, 16, 64, 128], [4, 24, 0]),
+                q_block_size=pick([8, 16, 64, 65, 128], [0, 1, 3]),
+                kv_block_size=pick([8, 16, 32, 64, 128, 192], [0, 24, 48, 96]),
+                max_seq_len_kv=pick([1, 500, M.MAX_SEQ_LEN], [0, M.MAX_SEQ_LEN + 1]),
+                mask_type=pick([0, 1], [2]), window_left=pick([-1, -1, 0, 7], [-2]),
+                qkv_dtype=pick([0], [1]), out_dtype=pick([0, 1], [2]),
+                num_cus=pick([80, 256], [0]))
+
+
+def test_bsa_plan_matches_spec():
+    rng = np.random.default_rng(0)
+    n_ok = 0
+    for _ in range(3000):
+        a = _rand_static(rng)
+        st_py, plan_py = M.bsa_plan(**a)
+        st_c, plan_c = _c_bsa_plan(a)
+        assert st_c == st_py, (a, st_c, st_py)
+        if st_c == 0:
+            n_ok += 1
+            for k, v in plan_py.items():
+                assert getattr(plan_c, k) == v, (k, a)
+    assert n_ok > 500
+
+
+def _bsa_args_from_case(case, num_cus=256):
+    B, Sq, Hq, Hkv, D, Pn, ps = case.dims
+    return dict(B=B, Sq=Sq, Hq=Hq, Hkv=Hkv, D=D, num_pages=Pn, page_size=ps,
+                q_block_size=case.q_block_size, kv_block_size=case.kv_block_size,
+                max_seq_len_kv=case.max_seq_len_kv, mask_type=1 if case.mask == "causal" else 0,
+                window_left=case.window_left, qkv_dtype=0, out_dtype=0, num_cus=num_cus)
+
+
+def _c_bsa_validate(plan, ip, ix, bip, bix, sl):
+    bad = C.Bad()
+    ip, ix, bip, bix, sl = (np.ascontiguousarray(x, dtype=np.int32) for x in (ip, ix, bip, bix, sl))
+    st = P.lib().bsa_validate(ctypes.byref(plan), ip.ctypes.data, ix.ctypes.data, ix.size,
+                              bip.ctypes.data, bix.ctypes.data, bix.size, sl.ctypes.data,
+                              ctypes.byref(bad))
+    return (st, bad.field, bad.index) if st == M.PKB_ERR_METADATA else (st, 0, -1)
+
+
+def _mutations(rng, case):
+    """Yield (ip, ix, bip, bix, sl) with one random corruption each."""
+    base = [case.kv_indptr.copy(), case.kv_indices.copy(), case.block_indptr.copy(),
+            case.block_indices.copy(), case.seq_lens.copy()]
+    yield [x.copy() for x in base]
+    for _ in range(60):
+        ip, ix, bip, bix, sl = [x.copy() for x in base]
+        kind = rng.integers(0, 9)
+        if kind == 0 and ix.size:
+            ix[rng.integers(0, ix.size)] = rng.choice([-1, case.k.shape[0], 10 ** 6])
+        elif kind == 1:
+            ip[rng.integers(0, ip.size)] += int(rng.choice([-3, -1, 1, 5]))
+        elif kind == 2:
+            sl[rng.integers(0, sl.size)] = rng.choice([-1, case.max_seq_len_kv + 1,
+                                                       case.max_seq_len_kv])
+        elif kind == 3 and bix.size:
+            bix[rng.integers(0, bix.size)] = rng.choice([-1, 10 ** 5])
+        elif kind == 4 and bix.size > 1:
+            i = rng.integers(1, bix.size)
+            bix[i] = bix[i - 1]                       # duplicate within a row (often)
+        elif kind == 5:
+            f = bip.reshape(-1)
+            f[rng.integers(0, f.size)] += int(rng.choice([-2, 1, 3]))
+        elif kind == 6:
+            sl[rng.integers(0, sl.size)] += 40         # may need more pages than owned
+        elif kind == 7:
+            f = bip.reshape(-1)
+            f[-1] = bix.size + 1
+        else:
+            ip[0] = 1
+        yield ip, ix, bip, bix, sl
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_bsa_validate_matches_spec(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 4))
+    case = W.make_bsa(200 + seed, B, int(rng.integers(4, 40)), 4, 2, 128,
+                      [int(x) for x in rng.integers(1, 90, size=B)], 8, 4,
+                      int(rng.choice([8, 16, 64])), mask="causal", p_sel=0.6,
+                      max_seq_len_kv=120)
+    a = _bsa_args_from_case(case)
+    st, plan = _c_bsa_plan(a)
+    assert st == 0
+    spec_args = dict(a, num_q_blocks=plan.num_q_blocks, num_kv_blocks=plan.num_kv_blocks)
+    n_bad = 0
+    for ip, ix, bip, bix, sl in _mutations(rng, case):
+        want = M.bsa_validate(spec_args, ip, ix, bip, bix, sl)
+        got = _c_bsa_validate(plan, ip, ix, bip, bix, sl)
+        assert got == want, (got, want)
+        n_bad += want[0] != 0
+    assert n_bad > 20
+
+
+def test_bsa_validate_accepts_generated_workloads():
+    for case in (W.tiny_bsa("dense"), W.tiny_bsa("causal")):
+        a = _bsa_args_from_case(case)
+        st, plan = _c_bsa_plan(a)
+        assert st == 0
+        got = _c_bsa_validate(plan, case.kv_indptr, case.kv_indices, case.block_indptr,
+                              case.block_indices, case.seq_lens)
+        assert got == (0, 0, -1)
+
+
+def test_window_requires_causal_and_static_rules():
+    base = dict(B=1, Sq=16, Hq=4, Hkv=1, D=128, num_pages=4, page_size=16, q_block_size=16,
+                kv_block_size=32, max_seq_len_kv=64, mask_type=0, window_left=-1, qkv_dtype=0,
+                out_dtype=0, num_cus=256)
+    assert _c_bsa_plan(base)[0] == 0
+    assert _c_bsa_plan(dict(base, window_left=3))[0] == M.PKB_ERR_ARG     # needs causal
+    assert _c_bsa_plan(dict(base, window_left=3, mask_type=1))[0] == 0
+    assert _c_bsa_plan(dict(base, kv_block_size=48))[0] == M.PKB_ERR_ARG
+    assert _c_bsa_plan(dict(base, kv_block_size=192))[0] == 0
+    assert _c_bsa_plan(dict(base, q_block_size=1, Hq=4, Hkv=2))[0] == M.PKB_ERR_ARG  # 1*2 % 8
+    assert _c_bsa_plan(dict(base, q_block_size=4, Hq=4, Hkv=2))[0] == 0              # 4*2 % 8
+    assert _c_bsa_plan(dict(base, max_seq_len_kv=M.MAX_SEQ_LEN))[0] == 0
+    assert _c_bsa_plan(dict(base, max_seq_len_kv=M.MAX_SEQ_LEN + 1))[0] == M.PKB_ERR_ARG
+    assert _c_bsa_plan(dict(base, D=64))[0] == M.PKB_ERR_UNSUPPORTED
+    assert _c_bsa_plan(dict(base, Hq=3, Hkv=2))[0] == M.PKB_ERR_SHAPE
+
+
+# ----------------------------------------------------------------------------- prefill
+
+def _prefill_args(B, total_q, width, mask_type=1, window_left=-1, page_size=32, D=128, Hq=32,
+                  Hkv=8, num_pages=1000):
+    return dict(B=B, Hq=Hq, Hkv=Hkv, D=D, num_pages=num_pages, page_size=page_size,
+                total_q=total_q, width=width, mask_type=mask_type, window_left=window_left,
+                qkv_dtype=0, out_dtype=0, num_cus=256)
+
+
+def _c_prefill(args, qo, sl):
+    a = C.PrefillStaticArgs(args["B"], args["Hq"], args["Hkv"], args["D"], args["num_pages"],
+                            args["page_size"], args["total_q"], args["width"], args["mask_type"],
+                            args["window_left"], args["qkv_dtype"], args["out_dtype"],
+                            args["num_cus"])
+    return P.paged_prefill_plan(a, qo, sl)
+
+
+@pytest.mark.parametrize("mask,w", [(1, -1), (1, 1024), (0, -1), (1, 0)])
+def test_prefill_worklist_matches_spec(mask, w):
+    for D in (128, 256):
+        case = W.batch_prefill(3, D=D, window_left=w)
+        args = _prefill_args(8, int(case.qo_indptr[-1]), case.block_tables.shape[1], mask, w, D=D,
+                             num_pages=case.k.shape[0])
+        st, plan_py, wl_py = M.prefill_plan(args, case.qo_indptr, case.seq_lens)
+        assert st == 0
+        plan_c, wl_c = _c_prefill(args, case.qo_indptr, case.seq_lens)
+        assert np.array_equal(wl_c, wl_py)
+        for k, v in plan_py.items():
+            assert getattr(plan_c, k) == v, k
+
+
+def _c_prefill_validate(args, qo, sl, bt):
+    a = C.PrefillStaticArgs(args["B"], args["Hq"], args["Hkv"], args["D"], args["num_pages"],
+                            args["page_size"], args["total_q"], args["width"], args["mask_type"],
+                            args["window_left"], args["qkv_dtype"], args["out_dtype"],
+                            args["num_cus"])
+    st, f, i = P.paged_prefill_validate(a, qo, sl, bt, raise_on_error=False)
+    return (st, f, i) if st == M.PKB_ERR_METADATA else (st, 0, -1)
+
+
+def test_prefill_validate_matches_spec():
+    rng = np.random.default_rng(5)
+    case = W.make_prefill(9, 3, [5, 17, 9], [3, 0, 40], 8, 2, 128, 16)
+    args = _prefill_args(3, int(case.qo_indptr[-1]), case.block_tables.shape[1], Hq=8, Hkv=2,
+                         page_size=16, num_pages=case.k.shape[0])
+    args_spec = dict(args, block_table_width=args["width"])
+    n_bad = 0
+    for t in range(150):
+        qo, sl, bt = case.qo_indptr.copy(), case.seq_lens.copy(), case.block_tables.copy()
+        k = t % 6
+        if t == 0:
+            pass
+        elif k == 0:
+            qo[rng.integers(0, qo.size)] += int(rng.choice([-2, 1]))
+        elif k == 1:
+            sl[rng.integers(0, sl.size)] = int(rng.choice([-1, 0, 2, 80]))
+        elif k == 2:
+            bt[rng.integers(0, bt.shape[0]), rng.integers(0, bt.shape[1])] = int(rng.choice([-1, 10 ** 4]))
+        elif k == 3:
+            sl[rng.integers(0, sl.size)] += 16 * bt.shape[1]
+        elif k == 4:
+            qo[-1] += 1
+        else:
+            bt[:, 0] = -5
+        want = M.prefill_validate(args_spec, qo, sl, bt, bt.shape[1])
+        got = _c_prefill_validate(args, qo, sl, bt)
+        assert got == want, (t, got, want)
+        n_bad += want[0] != 0
+    assert n_bad > 60
+
+
+# ----------------------------------------------------------------------------- decode
+
+def test_decode_policy_matches_spec():
+    rng = np.random.default_rng(1)
+    for _ in range(2000):
+        B = int(rng.integers(1, 300)); Hkv = int(rng.choice([1, 2, 8])); Hq = Hkv * int(rng.choice([1, 4, 8]))
+        D = int(rng.choice([128, 256, 64])); msl = int(rng.choice([1, 63, 64, 65, 4096, 8192, 131072, M.MAX_SEQ_LEN]))
+        ps = int(rng.choice([8, 16, 12])); cus = int(rng.choice([80, 256]))
+        st, nbytes, S, sl = M.decode_policy(B, Hq, Hkv, D, msl, ps, cus)
+        if st != 0:
+            nb = ctypes.c_size_t(); s = ctypes.c_int32(); l = ctypes.c_int32()
+            assert P.lib().paged_decode_workspace_size(B, Hq, Hkv, D, msl, ps, cus, ctypes.byref(nb),
+                                                       ctypes.byref(s), ctypes.byref(l)) == st
+            continue
+        if S > 65535:
+            continue
+        got = P.paged_decode_workspace_size(B, Hq, Hkv, D, msl, ps, cus)
+        assert got == (nbytes, S, sl)
+        assert S * sl >= msl and sl % 64 == 0
+
+
+def test_decode_validate_matches_spec():
+    rng = np.random.default_rng(2)
+    case = W.make_decode(10, 4, 8, 2, 128, [5, 40, 1, 77], 16, extra_pages=3)
+    n_bad = 0
+    for t in range(200):
+        ip, ix, sl = case.kv_indptr.copy(), case.kv_indices.copy(), case.seq_lens.copy()
+        k = t % 5
+        if t == 0:
+            pass
+        elif k == 0:
+            ix[rng.integers(0, ix.size)] = int(rng.choice([-1, case.k.shape[0]]))
+        elif k == 1:
+            ip[rng.integers(0, ip.size)] += int(rng.choice([-1, 1, 2]))
+        elif k == 2:
+            sl[rng.integers(0, sl.size)] = int(rng.choice([0, -3, 78, 200]))
+        elif k == 3:
+            sl[rng.integers(0, sl.size)] += 17
+        else:
+            ip[0] = -1
+        want = M.decode_validate(4, case.k.shape[0], 16, 100, ip, ix, sl)
+        st, f, i = P.paged_decode_validate(4, case.k.shape[0], 16, 100, ip, ix, sl,
+                                           raise_on_error=False)
+        got = (st, f, i) if st == M.PKB_ERR_METADATA else (st, 0, -1)
+        assert got == want, (t, got, want)
+        n_bad += want[0] != 0
+    assert n_bad > 80
+
+
+# ----------------------------------------------------------------------------- sage
+
+def test_sage_validate_matches_spec():
+    rng = np.random.default_rng(3)
+    for t in range(120):
+        B, H, Sq, Sk, cap = 2, 3, int(rng.integers(1, 300)), int(rng.integers(1, 400)), int(rng.integers(0, 6))
+        nqb, nkb = -(-Sq // 64), -(-Sk // 64)
+        idx = rng.integers(-1, nkb + 1, size=(B, H, nqb, max(cap, 1)))[..., :cap].astype(np.int32)
+        if rng.random() < 0.5:
+            for b in range(B):
+                for h in range(H):
+                    for r in range(nqb):
+                        k = min(cap, nkb)
+                        idx[b, h, r, :k] = rng.permutation(nkb)[:k]
+        nums = rng.integers(-1, cap + 2, size=(B, H, nqb)).astype(np.int32) if rng.random() < 0.6 else None
+        if nums is not None and rng.random() < 0.5:
+            nums = np.clip(nums, 0, min(cap, nkb)).astype(np.int32)
+        bsn = int(rng.integers(-1, cap + 2))
+        rank = int(rng.integers(0, 4))
+        bs = None if rank == 0 else rng.integers(-1, 66, size=[(nkb,), (B, nkb), (B, H, nkb)][rank - 1]).astype(np.int32)
+        uniform = bool(rng.random() < 0.3)
+        want = M.sage_validate(idx, cap, bsn, bs, nums, uniform, B, H, Sq, Sk)
+        st, f, i = P.bsa_sage_validate(idx, cap, bsn, bs, nums, uniform, B, H, Sq, Sk,
+                                       raise_on_error=False)
+        got = (st, f, i) if st == M.PKB_ERR_METADATA else (st, 0, -1)
+        assert got == want, (t, got, want)

@@ -1,0 +1,217 @@
+"""GPU parity of the bf16 attention kernels against the fp64 oracle.
+
+Small cases span several 64-key tiles and query tiles with ragged tails; the
+named workloads run at full size and are checked on sampled rows.  Bars: bf16
+out 2e-2, fp32 out 2e-3, LSE 2e-3 (absolute).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gen import workloads as W
+from tests.gpu_util import (TOL_BF16, TOL_F32, TOL_LSE, assert_close, f64, oracle_bsa,
+                            oracle_decode, oracle_prefill, run_bsa, run_decode, run_prefill)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- block-sparse
+
+@pytest.mark.parametrize("mask", ["dense", "causal"])
+def test_tiny_bsa(mask):
+    case = W.tiny_bsa(mask)
+    _say("tiny_bsa", mask)
+    out, lse = run_bsa(case)
+    ref_o, ref_l = oracle_bsa(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, lse32 = run_bsa(case, out_dtype=torch.float32)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
+    # the bf16 output agrees with the fp32 one to the bf16 bar
+    assert (out.float() - out32).abs().max().item() <= TOL_BF16
+
+
+BSA_SWEEP = [
+    # B, Sq, Hq, Hkv, D, seq_lens, ps, qbs, kvbs, mask, w, bits_p, extra
+    (2, 64, 4, 1, 128, [200, 333], 16, 16, 32, "causal", -1, 0.95, {}),
+    (2, 70, 8, 2, 128, [70, 190], 16, 8, 8, "dense", -1, None, {}),
+    (1, 100, 4, 4, 128, [300], 32, 8, 16, "causal", 37, 0.9, {}),
+    (3, 50, 8, 1, 128, [0, 55, 129], 8, 4, 64, "causal", -1, None, {"out_of_range": 1, "max_seq_len_kv": 400}),
+    (2, 96, 16, 2, 128, [500, 260], 64, 16, 128, "dense", -1, 0.8, {"allow_empty": True}),
+    (1, 130, 32, 8, 128, [700], 64, 64, 64, "causal", -1, 0.99, {}),
+    (2, 40, 2, 1, 256, [90, 123], 16, 4, 32, "causal", 20, 0.9, {}),
+    (1, 33, 8, 2, 256, [180], 32, 16, 192, "dense", -1, None, {}),
+    (2, 20, 1, 1, 128, [64, 8], 8, 8, 8, "dense", -1, 0.5, {"allow_empty": True}),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BSA_SWEEP)))
+def test_bsa_sweep(i):
+    B, Sq, Hq, Hkv, D, sl, ps, qbs, kvbs, mask, w, bits_p, extra = BSA_SWEEP[i]
+    _say("bsa_sweep", BSA_SWEEP[i])
+    case = W.make_bsa(300 + i, B, Sq, Hq, Hkv, D, sl, ps, qbs, kvbs, mask=mask, window_left=w,
+                      bits_p=bits_p, extra_pages=3, **extra)
+    out, lse = run_bsa(case)
+    ref_o, ref_l = oracle_bsa(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, _ = run_bsa(case, out_dtype=torch.float32, with_lse=False)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
+
+
+def test_bsa_empty_rows_exact():
+    case = W.make_bsa(41, 2, 32, 4, 1, 128, [100, 90], 16, 16, 32, mask="dense", p_sel=0.0,
+                      allow_empty=True)
+    case.block_indptr[:] = 0        # no row selects anything
+    case.block_indices = np.zeros(0, dtype=np.int32)
+    out, lse = run_bsa(case)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_bsa_poison_unused_memory():
+    """NaN in unreferenced pages and in slots past the live length changes nothing."""
+    case = W.make_bsa(42, 2, 48, 8, 2, 128, [77, 150], 16, 16, 32, mask="causal", bits_p=0.9,
+                      extra_pages=9)
+    ref, ref_l = run_bsa(case)
+    last = []
+    for b in range(2):
+        L = int(case.seq_lens[b])
+        pg = case.kv_indices[case.kv_indptr[b] + (L - 1) // 16]
+        last.append((int(pg), L % 16 if L % 16 else 16))
+    used = []
+    for b in range(2):
+        n = -(-int(case.seq_lens[b]) // 16)
+        used += list(case.kv_indices[case.kv_indptr[b]:case.kv_indptr[b] + n])
+    k2, v2 = W.poison_unused_pages(case.k, case.v, used, last)
+    out, lse = run_bsa(case, k=k2, v=v2)
+    assert torch.equal(out, ref) and torch.equal(lse, ref_l)
+
+
+def test_bsa_page_permutation_and_combined_cache_bit_identical():
+    case = W.make_bsa(43, 2, 64, 8, 2, 128, [210, 95], 16, 16, 32, mask="causal", bits_p=0.9,
+                      extra_pages=6)
+    ref, ref_l = run_bsa(case)
+    perm = np.random.default_rng(0).permutation(case.k.shape[0])
+    k2 = torch.empty_like(case.k); v2 = torch.empty_like(case.v)
+    k2[torch.from_numpy(perm)] = case.k
+    v2[torch.from_numpy(perm)] = case.v
+    out, lse = run_bsa(case, k=k2, v=v2, indices=perm[case.kv_indices].astype(np.int32))
+    assert torch.equal(out, ref) and torch.equal(lse, ref_l)
+    out_c, lse_c = run_bsa(case, combined=True)
+    assert torch.equal(out_c, ref) and torch.equal(lse_c, ref_l)
+
+
+def test_bsa_all_blocks_equals_prefill():
+    B, Sq, Hq, Hkv, D = 2, 96, 8, 2, 128
+    case = W.make_bsa(44, B, Sq, Hq, Hkv, D, [96, 250], 32, 32, 64, mask="causal", p_sel=1.0)
+    out, lse = run_bsa(case, out_dtype=torch.float32)
+    table = np.full((B, 8), -1, dtype=np.int32)
+    for b in range(B):
+        ids = case.kv_indices[case.kv_indptr[b]:case.kv_indptr[b + 1]]
+        table[b, :len(ids)] = ids
+    pc = W.PrefillCase(case.q.reshape(B * Sq, Hq, D), case.k, case.v,
+                       np.array([0, Sq, 2 * Sq], dtype=np.int32), table, case.seq_lens, "causal")
+    out_p, lse_p = run_prefill(pc, out_dtype=torch.float32)
+    assert (out.reshape(B * Sq, Hq, D) - out_p).abs().max().item() <= 1e-5
+    assert (lse - lse_p).abs().max().item() <= 1e-5
+
+
+def test_long_bsa_sampled():
+    """Full-size long-context block-sparse workload, sampled query tokens."""
+    case = W.long_bsa()
+    _say("long_bsa: generated")
+    out, lse = run_bsa(case)
+    rng = np.random.default_rng(7)
+    toks = [(int(b), int(i)) for b, i in zip(rng.integers(0, 4, 48), rng.integers(0, 8192, 48))]
+    toks += [(0, 0), (1, 63), (2, 64), (3, 8191), (0, 959), (1, 960)]
+    ref_o, ref_l = oracle_bsa(case, tokens=toks)
+    got_o = np.stack([f64(out[b, i]) for b, i in toks])
+    got_l = np.stack([f64(lse[b * 8192 + i]) for b, i in toks])
+    assert_close(got_o, ref_o, TOL_BF16, "out")
+    assert_close(got_l, ref_l, TOL_LSE, "lse")
+    assert torch.isfinite(out.float()).all()
+
+
+# ----------------------------------------------------------------------------- prefill
+
+PREFILL_SWEEP = [
+    # B, qlens, prefixes, Hq, Hkv, D, ps, mask, w
+    (3, [5, 130, 64], [0, 70, 300], 8, 2, 128, 16, "causal", -1),
+    (2, [200, 33], [100, 0], 32, 8, 128, 32, "causal", 50),
+    (2, [40, 77], [10, 20], 4, 4, 128, 64, "dense", -1),
+    (2, [129, 7], [257, 1], 8, 1, 256, 128, "causal", -1),
+    (1, [300], [0], 4, 2, 256, 32, "causal", 0),
+]
+
+
+@pytest.mark.parametrize("i", range(len(PREFILL_SWEEP)))
+def test_prefill_sweep(i):
+    B, ql, pf, Hq, Hkv, D, ps, mask, w = PREFILL_SWEEP[i]
+    _say("prefill_sweep", PREFILL_SWEEP[i])
+    case = W.make_prefill(400 + i, B, ql, pf, Hq, Hkv, D, ps, mask=mask, window_left=w,
+                          extra_pages=2, output_scale=0.75)
+    out, lse = run_prefill(case)
+    ref_o, ref_l = oracle_prefill(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, _ = run_prefill(case, out_dtype=torch.float32, with_lse=False)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
+
+
+@pytest.mark.parametrize("D,w", [(128, -1), (128, 1024), (256, -1)])
+def test_batch_prefill_sampled(D, w):
+    case = W.batch_prefill(3, D=D, window_left=w)
+    _say("batch_prefill", D, w, int(case.qo_indptr[-1]))
+    out, lse = run_prefill(case)
+    rng = np.random.default_rng(8)
+    T = int(case.qo_indptr[-1])
+    rows = sorted(set([int(x) for x in rng.integers(0, T, 64)] + [0, T - 1] +
+                      [int(x) for x in case.qo_indptr[1:-1]]))
+    ref_o, ref_l = oracle_prefill(case, rows=rows)
+    assert_close(f64(out[rows]), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse[rows]), ref_l, TOL_LSE, "lse")
+
+
+# ----------------------------------------------------------------------------- decode
+
+DECODE_SWEEP = [
+    # B, Hq, Hkv, D, seq_lens, ps, mask, w, num_cus
+    (4, 32, 8, 128, [1, 63, 64, 1000], 16, "dense", -1, 256),
+    (3, 8, 8, 128, [4097, 5, 300], 16, "causal", 100, 256),
+    (2, 16, 2, 256, [777, 2049], 32, "dense", -1, 256),
+    (5, 4, 1, 128, [129, 1, 2000, 64, 65], 8, "causal", 0, 8),
+    (2, 64, 1, 128, [333, 1024], 16, "dense", -1, 256),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DECODE_SWEEP)))
+def test_decode_sweep(i):
+    B, Hq, Hkv, D, sl, ps, mask, w, ncu = DECODE_SWEEP[i]
+    _say("decode_sweep", DECODE_SWEEP[i])
+    case = W.make_decode(500 + i, B, Hq, Hkv, D, sl, ps, mask=mask, window_left=w, extra_pages=2,
+                         bmm2_scale=1.25)
+    out, lse, S = run_decode(case, num_cus=ncu)
+    ref_o, ref_l = oracle_decode(case)
+    assert_close(f64(out), ref_o, TOL_BF16, f"out (splits={S})")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, _, _ = run_decode(case, out_dtype=torch.float32, num_cus=ncu)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
+    out_c, lse_c, _ = run_decode(case, combined=True, num_cus=ncu)
+    assert torch.equal(out_c, out) and torch.equal(lse_c, lse)
+
+
+def test_batch_decode_sampled():
+    case = W.batch_decode()
+    _say("batch_decode: generated", int(case.seq_lens.sum()))
+    out, lse, S = run_decode(case)
+    reqs = [0, 1, 17, 33, 63] + [int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens))]
+    ref_o, ref_l = oracle_decode(case, requests=reqs)
+    assert_close(f64(out[reqs]), ref_o, TOL_BF16, f"out (splits={S})")
+    assert_close(f64(lse[reqs]), ref_l, TOL_LSE, "lse")
+    assert torch.isfinite(out.float()).all()
