@@ -286,7 +286,8 @@ def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus):
     tps = cdiv(tiles, S)
     S = cdiv(tiles, tps)
     split_len = tps * KV_TILE
-    nbytes = 0 if S == 1 else B * Hq * S * (D + 2) * 4
+    counters = cdiv(B * Hkv * 4, 256) * 256          # arrival counters, then partials
+    nbytes = 0 if S == 1 else counters + B * Hq * S * (D + 2) * 4
     return PKB_OK, nbytes, S, split_len
 
 

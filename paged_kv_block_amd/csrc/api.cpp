@@ -170,7 +170,8 @@ int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv
   p.v = (const uint16_t*)v;
   p.out = out;
   p.lse = lse;
-  p.part = S > 1 ? (float*)workspace : nullptr;
+  p.counters = S > 1 ? (int*)workspace : nullptr;
+  p.part = S > 1 ? (float*)((char*)workspace + pkb::decode_counter_bytes(B, Hkv)) : nullptr;
   p.kv_indptr = kv_indptr;
   p.kv_indices = kv_indices;
   p.seq_lens = seq_lens;
@@ -192,21 +193,6 @@ int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv
   dim3 grid(S, Hkv, B);
   hipError_t e = pkb::launch_attn(p, D, 4, pkb::kModeDecode, grid, s);
   if (e != hipSuccess) return hip_status(e);
-  if (S > 1) {
-    pkb::MergeParams mp;
-    mp.part = (const float*)workspace;
-    mp.seq_lens = seq_lens;
-    mp.out = out;
-    mp.lse = lse;
-    mp.B = B;
-    mp.Hq = Hq;
-    mp.num_splits = S;
-    mp.split_len = split_len;
-    mp.out_f32 = p.out_f32;
-    mp.out_scale = bmm2_scale;
-    e = pkb::launch_decode_merge(mp, D, s);
-    if (e != hipSuccess) return hip_status(e);
-  }
   return PKB_OK;
 }
 

@@ -414,25 +414,66 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
   }
 
   // ---------------- epilogue ----------------
+  if (partial_out) {
+    // Split-KV decode: write this split's unnormalised partial (O, m, l), then
+    // count arrivals per (request, KV head).  The last split to arrive merges
+    // all partials and puts the counter back to zero, so a zeroed workspace
+    // stays zeroed between launches.
+    if (wave_rows) {
+      const float l_tot = half_sum(l_run);
+      if (row_ok) {
+        float* dst = p.part + (((int64_t)b * p.Hq + my_hq) * p.num_splits + split) * (D + 2);
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * d + 8 * g4 + 4 * hh;
+            f32x4 v4 = {oacc[d][4 * g4], oacc[d][4 * g4 + 1], oacc[d][4 * g4 + 2], oacc[d][4 * g4 + 3]};
+            *(f32x4*)(dst + d0) = v4;
+          }
+        if (hh == 0) {
+          dst[D] = m_run;
+          dst[D + 1] = l_tot;
+        }
+      }
+    }
+    __shared__ int s_last;
+    __threadfence();
+    __syncthreads();
+    int* counter = p.counters + (int64_t)b * p.Hkv + kvh;
+    const int n_live = (L + p.split_len - 1) / p.split_len;
+    if (tid == 0) s_last = (atomicAdd(counter, 1) == n_live - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    for (int e = tid; e < G * D; e += NT) {
+      const int r = e / D;
+      const int d = e - r * D;
+      const int hq = kvh * G + r;
+      const float* base = p.part + ((int64_t)b * p.Hq + hq) * p.num_splits * (D + 2);
+      float M = -INFINITY;
+      for (int s2 = 0; s2 < n_live; ++s2) M = fmaxf(M, base[s2 * (D + 2) + D]);
+      float lsum = 0.f, acc = 0.f;
+      if (M != -INFINITY) {
+        for (int s2 = 0; s2 < n_live; ++s2) {
+          const float w = fast_exp2(base[s2 * (D + 2) + D] - M);
+          lsum += base[s2 * (D + 2) + D + 1] * w;
+          acc += base[s2 * (D + 2) + d] * w;
+        }
+      }
+      const bool empty = !(lsum > 0.f);
+      const float o = empty ? 0.f : acc * (p.out_scale / lsum);
+      const int64_t orow = (int64_t)b * p.Hq + hq;
+      if (p.out_f32) ((float*)p.out)[orow * D + d] = o;
+      else ((__bf16*)p.out)[orow * D + d] = (__bf16)o;
+      if (p.lse && d == 0) p.lse[orow] = empty ? -INFINITY : (M + __log2f(lsum)) * kLn2;
+    }
+    if (tid == 0) atomicExch(counter, 0);
+    return;
+  }
   if (!wave_rows) return;
   const float l_tot = half_sum(l_run);
   if (!row_ok) return;
-  if (partial_out) {
-    float* dst = p.part + (((int64_t)b * p.Hq + my_hq) * p.num_splits + split) * (D + 2);
-#pragma unroll
-    for (int d = 0; d < NDB; ++d)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * d + 8 * g4 + 4 * hh;
-        f32x4 v4 = {oacc[d][4 * g4], oacc[d][4 * g4 + 1], oacc[d][4 * g4 + 2], oacc[d][4 * g4 + 3]};
-        *(f32x4*)(dst + d0) = v4;
-      }
-    if (hh == 0) {
-      dst[D] = m_run;
-      dst[D + 1] = l_tot;
-    }
-    return;
-  }
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_tot;
   const int64_t orow = ((int64_t)(tok_base + my_i) * p.Hq + my_hq);
@@ -462,46 +503,6 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
   }
   if (p.lse && hh == 0)
     p.lse[orow] = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
-}
-
-// Merge of split-KV partials: per (request, query head), LSE-weighted sum of the
-// partial outputs of its live splits (splits s < ceil(seq_len / split_len)).
-template <int D>
-__global__ void __launch_bounds__(64) decode_merge_kernel(const MergeParams p) {
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq;
-  const int L = p.seq_lens[b];
-  const int n = min(p.num_splits, (L + p.split_len - 1) / p.split_len);
-  const float* base = p.part + (int64_t)bh * p.num_splits * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, base[s * (D + 2) + D]);
-  float lsum = 0.f;
-  if (M != -INFINITY)
-    for (int s = 0; s < n; ++s) lsum += base[s * (D + 2) + D + 1] * fast_exp2(base[s * (D + 2) + D] - M);
-  const bool empty = !(lsum > 0.f);
-  const float inv = empty ? 0.f : p.out_scale / lsum;
-  constexpr int PER = D / 64;
-  float acc[PER];
-#pragma unroll
-  for (int t = 0; t < PER; ++t) acc[t] = 0.f;
-  if (!empty) {
-    for (int s = 0; s < n; ++s) {
-      const float w = fast_exp2(base[s * (D + 2) + D] - M);
-      if (w == 0.f) continue;
-#pragma unroll
-      for (int t = 0; t < PER; ++t) acc[t] += w * base[s * (D + 2) + threadIdx.x * PER + t];
-    }
-  }
-  if (p.out_f32) {
-    float* o = (float*)p.out + (int64_t)bh * D + threadIdx.x * PER;
-#pragma unroll
-    for (int t = 0; t < PER; ++t) o[t] = acc[t] * inv;
-  } else {
-    uint16_t* o = (uint16_t*)p.out + (int64_t)bh * D + threadIdx.x * PER;
-#pragma unroll
-    for (int t = 0; t < PER; t += 2) *(uint32_t*)(o + t) = pack_bf16x2(acc[t] * inv, acc[t + 1] * inv);
-  }
-  if (p.lse && threadIdx.x == 0) p.lse[bh] = empty ? -INFINITY : (M + __log2f(lsum)) * kLn2;
 }
 
 template <int D, int NW, int MODE>
@@ -535,15 +536,6 @@ hipError_t launch_attn(const AttnParams& p, int D, int waves, int mode, dim3 gri
                        hipStream_t stream) {
   if (D == 128) return launch_d<128>(p, waves, mode, grid, stream);
   if (D == 256) return launch_d<256>(p, waves, mode, grid, stream);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream) {
-  dim3 grid(p.B * p.Hq);
-  MergeParams arg = p;
-  void* args[] = {(void*)&arg};
-  if (D == 128) return hipLaunchKernel((const void*)decode_merge_kernel<128>, grid, dim3(64), args, 0, stream);
-  if (D == 256) return hipLaunchKernel((const void*)decode_merge_kernel<256>, grid, dim3(64), args, 0, stream);
   return hipErrorInvalidValue;
 }
 

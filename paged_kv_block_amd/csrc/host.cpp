@@ -289,7 +289,10 @@ int paged_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
   if (S > 65535) return PKB_ERR_UNSUPPORTED;
   if (num_splits) *num_splits = (int32_t)S;
   if (split_len) *split_len = (int32_t)(tps * tile);
-  if (bytes) *bytes = S == 1 ? 0 : (size_t)B * Hq * S * (D + 2) * sizeof(float);
+  // [B*Hkv] int32 arrival counters (rounded up to 256 B), then [B, Hq, S, D+2]
+  // fp32 partials.
+  const size_t counters = ((size_t)B * Hkv * 4 + 255) / 256 * 256;
+  if (bytes) *bytes = S == 1 ? 0 : counters + (size_t)B * Hq * S * (D + 2) * sizeof(float);
   return PKB_OK;
 }
 

@@ -20,6 +20,7 @@ struct AttnParams {
   void* out;                  // [tokens, Hq, D] bf16 or fp32
   float* lse;                 // [tokens, Hq] or null
   float* part;                // decode split partials [B, Hq, S, D+2] or null
+  int* counters;              // decode split arrival counters [B, Hkv] (zeroed)
   const int32_t* kv_indptr;   // CSR page IDs (bsa, decode)
   const int32_t* kv_indices;
   const int32_t* block_tables;  // row-strided table (prefill)
@@ -36,15 +37,6 @@ struct AttnParams {
   int num_splits, split_len;
   int out_f32;
   float scale_log2;   // softmax scale * log2(e)
-  float out_scale;
-};
-
-struct MergeParams {
-  const float* part;
-  const int32_t* seq_lens;
-  void* out;
-  float* lse;
-  int B, Hq, num_splits, split_len, out_f32;
   float out_scale;
 };
 
@@ -65,9 +57,13 @@ struct SageParams {
 };
 
 size_t attn_lds_bytes(int D);
+
+// Decode workspace: arrival counters first, then the partials.
+inline size_t decode_counter_bytes(int B, int Hkv) {
+  return ((size_t)B * Hkv * sizeof(int) + 255) / 256 * 256;
+}
 hipError_t launch_attn(const AttnParams& p, int D, int waves, int mode, dim3 grid,
                        hipStream_t stream);
-hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream);
 hipError_t launch_sage(const SageParams& p, hipStream_t stream);
 
 }  // namespace pkb

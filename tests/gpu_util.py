@@ -101,7 +101,7 @@ def run_decode(case, out_dtype=torch.bfloat16, combined=False, num_cus=None):
     ncu = num_cus if num_cus is not None else P.num_cus()
     nbytes, S, split_len = P.paged_decode_workspace_size(B, Hq, case.k.shape[1], D,
                                                          case.max_seq_len, case.k.shape[2], ncu)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=DEV)
     cache = torch.stack([case.k, case.v], dim=1).to(DEV) if combined else \
         (case.k.to(DEV), case.v.to(DEV))
     out = torch.empty(q.shape, dtype=out_dtype, device=DEV)
