@@ -149,7 +149,7 @@ def bench_decode(steps, warmup, W, P):
            "kv_bytes_per_step": kv_bytes}
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "attn_fwd_kernel<128,4,decode> (split-KV + fused merge)",
+            "kernel": "decode_kernel<128> + decode_merge_kernel<128> (one step)",
             "per_unit": "4096 B of K+V per live token (Hkv=8, D=128, bf16)"}
     return case, gbs, ms_step, cfg, roof
 

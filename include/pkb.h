@@ -252,12 +252,11 @@ int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
 /* ======================================================================== */
 
 /* Static policy from max_seq_len (the page selects its policy from the static
- * maximum): the number of KV splits per (request, KV head), the split length
- * in tokens, and the workspace bytes paged_decode_run needs (0 when one split
- * suffices).  Workspace layout: ceil(B*Hkv*4/256)*256 bytes of int32 arrival
- * counters, then fp32 partials [B, Hq, num_splits, D+2].  As the page requires,
- * the workspace must be zero-initialised before its first use (and again after
- * the policy changes); every completed launch leaves the counters at zero. */
+ * maximum): each request's keys are cut into chunks of split_len tokens (at
+ * most num_splits chunks); workspace bytes paged_decode_run needs (0 when one
+ * chunk suffices): fp32 partials [B, Hq, num_splits, D+4] (O, running max,
+ * running sum, pad).  Every live partial is written before it is read, so the
+ * workspace needs no initialisation (zeroing it, as the page asks, is harmless). */
 int paged_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                 int32_t max_seq_len, int32_t page_size, int32_t num_cus,
                                 size_t* bytes, int32_t* num_splits, int32_t* split_len);
@@ -275,9 +274,8 @@ int paged_decode_validate(int32_t B, int32_t num_pages, int32_t page_size,
 /* Trusted run.  query [B, Hq, D] bf16; k/v pools as above; bmm1_scale is the
  * softmax scale (<= 0 selects 1/sqrt(D)); bmm2_scale multiplies the output;
  * out [B, Hq, D] (out_dtype), lse [B, Hq] fp32 or NULL; workspace of at least
- * paged_decode_workspace_size() bytes, zero-initialised before first use and
- * exclusive to this launch until it ends.  The last split of each (request,
- * KV head) to finish merges the partials in the same kernel. */
+ * paged_decode_workspace_size() bytes, exclusive to this launch until it ends.
+ * With more than one split a second, small kernel merges the partials. */
 int paged_decode_run(const void* query, const void* k, const void* v,
                      int64_t kv_page_stride, int64_t kv_head_stride,
                      const int32_t* paged_kv_indptr, const int32_t* paged_kv_indices,

@@ -269,8 +269,10 @@ def prefill_plan(args, qo_indptr, seq_lens):
 # ----------------------------------------------------------------------------
 
 def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus):
-    """Split-KV policy from the static maximum length.  Returns
-    (status, bytes, num_splits, split_len)."""
+    """Chunk (split) policy from the static maximum length: chunk length CH
+    starts at 1024 tokens (doubled while a request would need > 4096 chunks),
+    then halves down to 64 until B*Hkv*ceil(max_seq_len/CH) >= 8 items per
+    persistent wave (4 waves per CU).  Returns (status, bytes, chunks, CH)."""
     if min(B, Hq, Hkv, num_cus) < 1 or page_size < 1:
         return PKB_ERR_ARG, 0, 0, 0
     if Hq % Hkv:
@@ -279,15 +281,15 @@ def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus):
         return PKB_ERR_UNSUPPORTED, 0, 0, 0
     if not (1 <= max_seq_len <= MAX_SEQ_LEN):
         return PKB_ERR_ARG, 0, 0, 0
-    tiles = cdiv(max_seq_len, KV_TILE)
-    items = B * Hkv
-    target = 16 * num_cus
-    S = min(max(cdiv(target, items), 1), tiles)
-    tps = cdiv(tiles, S)
-    S = cdiv(tiles, tps)
-    split_len = tps * KV_TILE
-    counters = cdiv(B * Hkv * 4, 256) * 256          # arrival counters, then partials
-    nbytes = 0 if S == 1 else counters + B * Hq * S * (D + 2) * 4
+    CH = 1024
+    while cdiv(max_seq_len, CH) > 4096:
+        CH *= 2
+    waves = 4 * num_cus
+    while CH > 64 and B * Hkv * cdiv(max_seq_len, CH) < 8 * waves:
+        CH //= 2
+    S = cdiv(max_seq_len, CH)
+    split_len = CH
+    nbytes = 0 if S == 1 else B * Hq * S * (D + 4) * 4   # fp32 partials (O, m, l, pad)
     return PKB_OK, nbytes, S, split_len
 
 

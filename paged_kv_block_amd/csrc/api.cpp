@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/pkb.h"
@@ -163,36 +165,83 @@ int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv
     return PKB_ERR_SHAPE;
   if (!isfinite(bmm2_scale)) return PKB_ERR_ARG;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKB_ERR_WORKSPACE;
-  AttnParams p;
-  memset(&p, 0, sizeof(p));
-  p.q = (const uint16_t*)query;
-  p.k = (const uint16_t*)k;
-  p.v = (const uint16_t*)v;
-  p.out = out;
-  p.lse = lse;
-  p.counters = S > 1 ? (int*)workspace : nullptr;
-  p.part = S > 1 ? (float*)((char*)workspace + pkb::decode_counter_bytes(B, Hkv)) : nullptr;
-  p.kv_indptr = kv_indptr;
-  p.kv_indices = kv_indices;
-  p.seq_lens = seq_lens;
-  p.kv_page_stride = kv_page_stride;
-  p.kv_head_stride = kv_head_stride;
-  p.B = B;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.G = Hq / Hkv;
-  p.page_size = page_size;
-  p.causal = mask_type == PKB_MASK_CAUSAL;
-  p.window_left = window_left;
-  p.num_splits = S;
-  p.split_len = split_len;
-  p.out_f32 = out_dtype == PKB_FP32;
-  p.scale_log2 = scale_or_default(bmm1_scale, D) * 1.4426950408889634f;
-  p.out_scale = bmm2_scale;
   const hipStream_t s = (hipStream_t)stream;
   dim3 grid(S, Hkv, B);
-  hipError_t e = pkb::launch_attn(p, D, 4, pkb::kModeDecode, grid, s);
-  if (e != hipSuccess) return hip_status(e);
+  float* part = S > 1 ? (float*)workspace : nullptr;
+  const float sl2 = scale_or_default(bmm1_scale, D) * 1.4426950408889634f;
+  if (Hq / Hkv <= pkb::kDecodeMaxGroup) {
+    pkb::DecodeParams d;
+    memset(&d, 0, sizeof(d));
+    d.q = (const uint16_t*)query;
+    d.k = (const uint16_t*)k;
+    d.v = (const uint16_t*)v;
+    d.out = out;
+    d.lse = lse;
+    d.part = part;
+    d.kv_indptr = kv_indptr;
+    d.kv_indices = kv_indices;
+    d.seq_lens = seq_lens;
+    d.kv_page_stride = kv_page_stride;
+    d.kv_head_stride = kv_head_stride;
+    d.B = B;
+    d.Hq = Hq;
+    d.Hkv = Hkv;
+    d.G = Hq / Hkv;
+    d.page_size = page_size;
+    d.window_left = window_left;
+    d.num_splits = S;
+    d.split_len = split_len;
+    d.out_f32 = out_dtype == PKB_FP32;
+    d.scale_log2 = sl2;
+    d.out_scale = bmm2_scale;
+    const int64_t items = (int64_t)B * Hkv * S;
+    const int waves = (int)std::min<int64_t>(items, (int64_t)num_cus * pkb::kDecodeWavesPerCu);
+    hipError_t e = pkb::launch_decode(d, D, waves, s);
+    if (e != hipSuccess) return hip_status(e);
+  } else {
+    // Larger GQA groups: the general attention kernel in split-KV decode mode.
+    AttnParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = (const uint16_t*)query;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.out = out;
+    p.lse = lse;
+    p.part = part;
+    p.kv_indptr = kv_indptr;
+    p.kv_indices = kv_indices;
+    p.seq_lens = seq_lens;
+    p.kv_page_stride = kv_page_stride;
+    p.kv_head_stride = kv_head_stride;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.page_size = page_size;
+    p.causal = mask_type == PKB_MASK_CAUSAL;
+    p.window_left = window_left;
+    p.num_splits = S;
+    p.split_len = split_len;
+    p.out_f32 = out_dtype == PKB_FP32;
+    p.scale_log2 = sl2;
+    p.out_scale = bmm2_scale;
+    hipError_t e = pkb::launch_attn(p, D, 4, pkb::kModeDecode, grid, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (S > 1) {
+    pkb::MergeParams mp;
+    mp.part = part;
+    mp.seq_lens = seq_lens;
+    mp.out = out;
+    mp.lse = lse;
+    mp.B = B;
+    mp.Hq = Hq;
+    mp.num_splits = S;
+    mp.split_len = split_len;
+    mp.out_f32 = out_dtype == PKB_FP32;
+    mp.out_scale = bmm2_scale;
+    return hip_status(pkb::launch_decode_merge(mp, D, s));
+  }
   return PKB_OK;
 }
 

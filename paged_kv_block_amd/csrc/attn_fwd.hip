@@ -415,60 +415,24 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
 
   // ---------------- epilogue ----------------
   if (partial_out) {
-    // Split-KV decode: write this split's unnormalised partial (O, m, l), then
-    // count arrivals per (request, KV head).  The last split to arrive merges
-    // all partials and puts the counter back to zero, so a zeroed workspace
-    // stays zeroed between launches.
-    if (wave_rows) {
-      const float l_tot = half_sum(l_run);
-      if (row_ok) {
-        float* dst = p.part + (((int64_t)b * p.Hq + my_hq) * p.num_splits + split) * (D + 2);
+    // Split-KV decode: this split's unnormalised partial (O, m, l); a separate
+    // merge kernel combines the splits.
+    if (!wave_rows) return;
+    const float l_tot = half_sum(l_run);
+    if (!row_ok) return;
+    float* dst = p.part + (((int64_t)b * p.Hq + my_hq) * p.num_splits + split) * (D + 4);
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = 32 * d + 8 * g4 + 4 * hh;
-            f32x4 v4 = {oacc[d][4 * g4], oacc[d][4 * g4 + 1], oacc[d][4 * g4 + 2], oacc[d][4 * g4 + 3]};
-            *(f32x4*)(dst + d0) = v4;
-          }
-        if (hh == 0) {
-          dst[D] = m_run;
-          dst[D + 1] = l_tot;
-        }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * d + 8 * g4 + 4 * hh;
+        f32x4 v4 = {oacc[d][4 * g4], oacc[d][4 * g4 + 1], oacc[d][4 * g4 + 2], oacc[d][4 * g4 + 3]};
+        *(f32x4*)(dst + d0) = v4;
       }
+    if (hh == 0) {
+      dst[D] = m_run;
+      dst[D + 1] = l_tot;
     }
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    int* counter = p.counters + (int64_t)b * p.Hkv + kvh;
-    const int n_live = (L + p.split_len - 1) / p.split_len;
-    if (tid == 0) s_last = (atomicAdd(counter, 1) == n_live - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int e = tid; e < G * D; e += NT) {
-      const int r = e / D;
-      const int d = e - r * D;
-      const int hq = kvh * G + r;
-      const float* base = p.part + ((int64_t)b * p.Hq + hq) * p.num_splits * (D + 2);
-      float M = -INFINITY;
-      for (int s2 = 0; s2 < n_live; ++s2) M = fmaxf(M, base[s2 * (D + 2) + D]);
-      float lsum = 0.f, acc = 0.f;
-      if (M != -INFINITY) {
-        for (int s2 = 0; s2 < n_live; ++s2) {
-          const float w = fast_exp2(base[s2 * (D + 2) + D] - M);
-          lsum += base[s2 * (D + 2) + D + 1] * w;
-          acc += base[s2 * (D + 2) + d] * w;
-        }
-      }
-      const bool empty = !(lsum > 0.f);
-      const float o = empty ? 0.f : acc * (p.out_scale / lsum);
-      const int64_t orow = (int64_t)b * p.Hq + hq;
-      if (p.out_f32) ((float*)p.out)[orow * D + d] = o;
-      else ((__bf16*)p.out)[orow * D + d] = (__bf16)o;
-      if (p.lse && d == 0) p.lse[orow] = empty ? -INFINITY : (M + __log2f(lsum)) * kLn2;
-    }
-    if (tid == 0) atomicExch(counter, 0);
     return;
   }
   if (!wave_rows) return;

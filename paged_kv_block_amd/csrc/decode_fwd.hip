@@ -1,0 +1,384 @@
+// decode_fwd.hip -- single-token paged decode (split-KV + merge) for gfx950.
+//
+// What is computed (FlashInfer page "prims_ts_batch_decode_with_kv_cache"): for
+// request b and query head h, out = bmm2_scale * softmax(bmm1_scale * q.K^T) V
+// over keys j < seq_len[b] (and j >= seq_len-1-w with a left window w >= 0),
+// plus the natural-log LSE.
+//
+// The path is bound by HBM bandwidth -- every live K/V byte is read once -- so
+// the design is about keeping bytes in flight on every CU until the end:
+//   * Work items are equal-size chunks: (request, chunk of CH tokens, KV head).
+//     The grid is persistent (a fixed number of single-wave workgroups); wave w
+//     takes items w, w + W, w + 2W, ... of the flattened list, which it derives
+//     on the device from seq_lens (no host read), so long and short requests
+//     spread evenly and no CU idles while a long request finishes.
+//   * Inside an item, keys go in groups of 32.  S^T = K Q^T uses
+//     v_mfma_f32_16x16x32_bf16 with M = 16 keys, N = the GQA group (up to 16
+//     query heads), K = 32 head dims; the A operand (16 keys x 32 dims) is
+//     loaded straight from the page pool into registers, each lane reading 16
+//     contiguous bytes of one key row.
+//   * V (32 keys x D) is copied row-major into the wave's LDS slab and read back
+//     with ds_read_b64_tr_b16, which delivers a 4-key x 16-dim block column-wise:
+//     the A operand of O^T += V^T P^T.  Lane group g then holds keys {4g..4g+3}
+//     of the first 16-key unit and {16+4g..16+4g+3} of the second -- the key set
+//     its S^T accumulator already holds -- so P^T feeds the MFMA directly.
+//   * Software pipeline: group j+1's loads are in flight while group j computes
+//     (two groups per wave in registers); page IDs are translated two ahead.
+// Each item writes a partial (O, m, l); a small second kernel merges the chunks
+// of every (request, head).  A kernel boundary, not an in-kernel agent-scope
+// fence, makes the partials visible: on this part such a fence writes back and
+// invalidates the whole L2 of an XCD.
+#include "device_common.h"
+#include "pkb_internal.h"
+
+namespace pkb {
+
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+
+template <int D>
+struct DecLayout {
+  static constexpr int KEYS = 32;              // keys per wave iteration
+  static constexpr int VROW = D * 2 + 32;      // V row bytes in LDS; the pad puts the four
+                                               // rows of one transpose read on distinct banks
+  static constexpr int LDS = KEYS * VROW;
+  static constexpr int PIECES = KEYS * D / 8;  // 16-byte pieces of V per group
+};
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
+  using Lay = DecLayout<D>;
+  constexpr int KS = D / 32;             // MFMA k-steps over the head dim (S^T)
+  constexpr int DB = D / 16;             // 16-row blocks of O^T
+  constexpr int VP = Lay::PIECES / 64;   // V pieces per lane per group
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* vs = smem;
+
+  const int lane = threadIdx.x;
+  const int g = lane >> 4;               // lane group: 4 keys of each 16-key unit
+  const int qn = lane & 15;              // MFMA column = query head in the group
+  const int G = p.G;
+  const int CH = p.split_len;
+  const int S = p.num_splits;
+
+  // running position in the flattened (request, chunk) list
+  int blk = 0;            // current block of 64 requests
+  int blk_base = 0;       // chunks before this block
+  int n_b = 0, incl = 0;  // this lane's request: chunk count, inclusive prefix in block
+  auto load_block = [&]() {
+    const int bb = blk * 64 + lane;
+    n_b = bb < p.B ? (p.seq_lens[bb] + CH - 1) / CH : 0;
+    incl = wave_incl_scan(n_b);
+  };
+  load_block();
+
+  const int W = gridDim.x;
+  for (int item = blockIdx.x;; item += W) {
+    const int j = item / p.Hkv;              // flattened (request, chunk)
+    const int kvh = item - j * p.Hkv;
+    // advance to the block of requests that holds chunk j
+    int tot = readlane_i32(incl, 63);
+    while (j >= blk_base + tot && blk * 64 + 64 < p.B) {
+      blk_base += tot;
+      ++blk;
+      load_block();
+      tot = readlane_i32(incl, 63);
+    }
+    if (j >= blk_base + tot) break;          // past the last chunk: done
+    const int local = j - blk_base;
+    const unsigned long long msk = __ballot(incl > local);
+    const int ln = __builtin_ctzll(msk);
+    const int b = blk * 64 + ln;
+    const int c = local - (readlane_i32(incl, ln) - readlane_i32(n_b, ln));
+
+    const int L = p.seq_lens[b];
+    int k_lo = p.window_left >= 0 ? max(0, L - 1 - p.window_left) : 0;
+    k_lo = max(k_lo, c * CH);
+    const int k_hi = min(L, (c + 1) * CH);
+    const int t_base = k_lo & ~31;
+    const int n_groups = k_hi > k_lo ? (k_hi - t_base + 31) >> 5 : 0;
+    const int64_t head_off = (int64_t)kvh * p.kv_head_stride;
+    const int32_t* ids = p.kv_indices + p.kv_indptr[b];
+
+    bf16x8 qf[KS];
+    {
+      const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + kvh * G + qn) * D + 8 * g;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (qn < G) x = ld_global_16(qrow + 32 * s);
+        qf[s] = as_bf16x8(x);
+      }
+    }
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // element offset of the 8-token chunk (lanes 0..3: four chunks of a group)
+    auto chunk_off = [&](int grp) -> int64_t {
+      int64_t off = 0;
+      const int t = t_base + grp * 32 + 8 * (lane & 3);
+      if (lane < 4 && grp < n_groups && t < L) {
+        const int pi = t / p.page_size;
+        off = (int64_t)ids[pi] * p.kv_page_stride + head_off + (int64_t)(t - pi * p.page_size) * D;
+      }
+      return off;
+    };
+
+    const char* kbase = (const char*)p.k;
+    const char* vbase = (const char*)p.v;
+    // Loads of one 32-key group.  K goes straight into the A operand of S^T;
+    // V pieces are row-major (piece lane + 64i is key 4i + lane/16 at D = 128,
+    // 2i + lane/32 at D = 256, so each load's chunk is wave-uniform).  Dead
+    // chunks have offset 0 (page 0, always in bounds); their keys are masked.
+    auto load_group = [&](int64_t off_v, bf16x8 (&ka)[2][KS], u32x4 (&vr)[VP]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t o0 = readlane_i64(off_v, 2 * u), o1 = readlane_i64(off_v, 2 * u + 1);
+        const int64_t off = (qn < 8 ? o0 : o1) * 2 + ((qn & 7) * D + 8 * g) * 2;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ka[u][s] = as_bf16x8(ld_global_16(kbase + off + 64 * s));
+      }
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const int piece = lane + 64 * i;
+        const int key = piece / (D / 8);
+        const int dp = piece - key * (D / 8);
+        const int64_t off = readlane_i64(off_v, (64 * i) / (D / 8) / 8) * 2 + ((key & 7) * D + dp * 8) * 2;
+        vr[i] = ld_global_16(vbase + off);
+      }
+    };
+
+    // Software pipeline: group j+1 is in flight while group j computes; page
+    // translation runs two groups ahead.
+    bf16x8 ka[2][KS], ka_n[2][KS];
+    u32x4 vr[VP], vr_n[VP];
+    load_group(chunk_off(0), ka, vr);
+    int64_t nxt = chunk_off(1);
+    for (int grp = 0; grp < n_groups; ++grp) {
+      const int t0 = t_base + grp * 32;
+      const bool full = t0 >= k_lo && t0 + 32 <= k_hi;
+      // page IDs first: vmcnt retires in issue order, so the wait for this load
+      // (next iteration) must not also wait for the group loads issued after it
+      const int64_t nn = chunk_off(grp + 2);
+      if (grp + 1 < n_groups) load_group(nxt, ka_n, vr_n);
+      nxt = nn;
+
+      f32x4 sacc[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][s], qf[s], sacc[u], 0, 0, 0);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sv = sacc[u][i] * p.scale_log2;
+          if (!full) {
+            const int t = t0 + 16 * u + 4 * g + i;
+            sv = (t >= k_lo && t < k_hi) ? sv : -INFINITY;
+          }
+          sacc[u][i] = sv;
+          mx = fmaxf(mx, sv);
+        }
+      if (!full) {
+        // dead keys contribute nothing: zero their V rows (no 0 * NaN)
+#pragma unroll
+        for (int i = 0; i < VP; ++i) {
+          const int key = (lane + 64 * i) / (D / 8);
+          const int t = t0 + key;
+          if (!(t >= k_lo && t < k_hi)) vr[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      mx = quad_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fast_exp2(sacc[u][i] - m_use);
+          sacc[u][i] = e;
+          ps += e;
+        }
+      if (m_new != m_run) {            // rescale only when some running max moved
+        const float alpha = fast_exp2(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
+      }
+      l_run += ps;
+      m_run = m_new;
+
+      // V slab -> LDS, then O^T += V^T P^T
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const int piece = lane + 64 * i;
+        const int key = piece / (D / 8);
+        const int dp = piece - key * (D / 8);
+        *(u32x4*)(vs + key * Lay::VROW + dp * 16) = vr[i];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      u32x4 pw;
+      pw[0] = pack_bf16x2(sacc[0][0], sacc[0][1]);
+      pw[1] = pack_bf16x2(sacc[0][2], sacc[0][3]);
+      pw[2] = pack_bf16x2(sacc[1][0], sacc[1][1]);
+      pw[3] = pack_bf16x2(sacc[1][2], sacc[1][3]);
+      u32x4 plo = {0u, 0u, 0u, 0u};
+      if (p.out_f32) {
+        // fp32 output: P - bf16(P) enters as a second operand (~16-bit P)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f32x4& sa = sacc[t >> 1];
+          const int i0 = 2 * (t & 1);
+          plo[t] = pack_bf16x2(sa[i0] - __uint_as_float(pw[t] << 16),
+                               sa[i0 + 1] - __uint_as_float(pw[t] & 0xFFFF0000u));
+        }
+      }
+      // transpose-read addresses: lane (4r + c) of a 16-lane group reads row
+      // 4g + r (unit 0) or 16 + 4g + r (unit 1), dims 16d + 4c .. +3
+      const int rr = (lane & 15) >> 2, cc = lane & 3;
+      const unsigned char* a0 = vs + (4 * g + rr) * Lay::VROW + 8 * cc;
+      const unsigned char* a1 = vs + (16 + 4 * g + rr) * Lay::VROW + 8 * cc;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(a0 + 32 * d));
+        const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(a1 + 32 * d));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, x0);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, x1);
+        u32x4 aw;
+        aw[0] = w0[0]; aw[1] = w0[1]; aw[2] = w1[0]; aw[3] = w1[1];
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), as_bf16x8(pw), oacc[d], 0, 0, 0);
+        if (p.out_f32)
+          oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), as_bf16x8(plo), oacc[d], 0, 0, 0);
+      }
+      // the slab is rewritten next iteration: keep these reads before those writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ka[u][s] = ka_n[u][s];
+#pragma unroll
+      for (int i = 0; i < VP; ++i) vr[i] = vr_n[i];
+    }
+
+    // ---- item result: lane (qn, g) holds O^T rows 16d + 4g + i of head qn ----
+    const float l_tot = quad_sum(l_run);
+    if (qn < G) {
+      const int hq = kvh * G + qn;
+      if (S > 1) {
+        float* dst = p.part + (((int64_t)b * p.Hq + hq) * S + c) * (D + 4);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) *(f32x4*)(dst + 16 * d + 4 * g) = oacc[d];
+        if (g == 0) {
+          dst[D] = m_run;
+          dst[D + 1] = l_tot;
+        }
+      } else {
+        const bool empty = !(l_tot > 0.f);
+        const float inv = empty ? 0.f : p.out_scale / l_tot;
+        const int64_t orow = (int64_t)b * p.Hq + hq;
+        if (p.out_f32) {
+          float* o = (float*)p.out + orow * D;
+#pragma unroll
+          for (int d = 0; d < DB; ++d) *(f32x4*)(o + 16 * d + 4 * g) = oacc[d] * inv;
+        } else {
+          uint16_t* o = (uint16_t*)p.out + orow * D;
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            u32x2 w;
+            w[0] = pack_bf16x2(oacc[d][0] * inv, oacc[d][1] * inv);
+            w[1] = pack_bf16x2(oacc[d][2] * inv, oacc[d][3] * inv);
+            *(u32x2*)(o + 16 * d + 4 * g) = w;
+          }
+        }
+        if (p.lse && g == 0) p.lse[orow] = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
+      }
+    }
+  }
+}
+
+// Merge of the chunk partials, one workgroup per (request, query head): LSE-
+// weighted sum over chunks c < ceil(seq_len / CH), in chunk order.
+template <int D>
+__global__ void __launch_bounds__(64) decode_merge_kernel(const MergeParams p) {
+  const int bh = blockIdx.x;
+  const int b = bh / p.Hq;
+  const int L = p.seq_lens[b];
+  const int n = min(p.num_splits, (L + p.split_len - 1) / p.split_len);
+  const float* base = p.part + (int64_t)bh * p.num_splits * (D + 4);
+  float M = -INFINITY;
+  for (int s = 0; s < n; ++s) M = fmaxf(M, base[s * (D + 4) + D]);
+  float lsum = 0.f;
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) acc[t] = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n; ++s) {
+      const float w = fast_exp2(base[s * (D + 4) + D] - M);
+      lsum += base[s * (D + 4) + D + 1] * w;
+#pragma unroll
+      for (int t = 0; t < PER; ++t) acc[t] += w * base[s * (D + 4) + threadIdx.x * PER + t];
+    }
+  }
+  const bool empty = !(lsum > 0.f);
+  const float inv = empty ? 0.f : p.out_scale / lsum;
+  if (p.out_f32) {
+    float* o = (float*)p.out + (int64_t)bh * D + threadIdx.x * PER;
+#pragma unroll
+    for (int t = 0; t < PER; ++t) o[t] = acc[t] * inv;
+  } else {
+    uint16_t* o = (uint16_t*)p.out + (int64_t)bh * D + threadIdx.x * PER;
+#pragma unroll
+    for (int t = 0; t < PER; t += 2) *(uint32_t*)(o + t) = pack_bf16x2(acc[t] * inv, acc[t + 1] * inv);
+  }
+  if (p.lse && threadIdx.x == 0) p.lse[bh] = empty ? -INFINITY : (M + __log2f(lsum)) * kLn2;
+}
+
+template <int D>
+static hipError_t launch_dec(const DecodeParams& p, int grid, hipStream_t st) {
+  DecodeParams arg = p;
+  void* args[] = {(void*)&arg};
+  return hipLaunchKernel((const void*)decode_kernel<D>, dim3(grid), dim3(64), args,
+                         DecLayout<D>::LDS, st);
+}
+
+hipError_t launch_decode(const DecodeParams& p, int D, int grid, hipStream_t stream) {
+  if (D == 128) return launch_dec<128>(p, grid, stream);
+  if (D == 256) return launch_dec<256>(p, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream) {
+  dim3 grid(p.B * p.Hq);
+  MergeParams arg = p;
+  void* args[] = {(void*)&arg};
+  if (D == 128) return hipLaunchKernel((const void*)decode_merge_kernel<128>, grid, dim3(64), args, 0, stream);
+  if (D == 256) return hipLaunchKernel((const void*)decode_merge_kernel<256>, grid, dim3(64), args, 0, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkb

@@ -52,6 +52,18 @@ __device__ __forceinline__ float half_sum(float x) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
+// Combine lanes l, l^16, l^32, l^48 (the four 16-lane groups).
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+  return half_max(x);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(r[0]) + __int_as_float(r[1]);
+  return half_sum(x);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Two floats -> packed bf16 pair (round to nearest even), low half = a.

@@ -279,20 +279,18 @@ int paged_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
   if (Hq % Hkv) return PKB_ERR_SHAPE;
   if ((D != 128 && D != 256) || page_size % 8) return PKB_ERR_UNSUPPORTED;
   if (max_seq_len < 1 || max_seq_len > PKB_MAX_SEQ_LEN) return PKB_ERR_ARG;
-  const int64_t tile = 64;
-  const int64_t tiles = cdiv(max_seq_len, tile);
-  const int64_t items = (int64_t)B * Hkv;
-  const int64_t target = 16LL * num_cus;
-  int64_t S = std::min(std::max<int64_t>(cdiv(target, items), 1), tiles);
-  const int64_t tps = cdiv(tiles, S);
-  S = cdiv(tiles, tps);
-  if (S > 65535) return PKB_ERR_UNSUPPORTED;
+  // Chunk length CH (tokens per work item): start at 1024 (grown while a request
+  // would need more than 4096 chunks), then halve down to 64 until the largest
+  // possible item count reaches 8 items per persistent wave (4 waves per CU).
+  int64_t CH = 1024;
+  while (cdiv(max_seq_len, CH) > 4096) CH *= 2;
+  const int64_t waves = 4LL * num_cus;
+  while (CH > 64 && (int64_t)B * Hkv * cdiv(max_seq_len, CH) < 8 * waves) CH /= 2;
+  const int64_t S = cdiv(max_seq_len, CH);
   if (num_splits) *num_splits = (int32_t)S;
-  if (split_len) *split_len = (int32_t)(tps * tile);
-  // [B*Hkv] int32 arrival counters (rounded up to 256 B), then [B, Hq, S, D+2]
-  // fp32 partials.
-  const size_t counters = ((size_t)B * Hkv * 4 + 255) / 256 * 256;
-  if (bytes) *bytes = S == 1 ? 0 : counters + (size_t)B * Hq * S * (D + 2) * sizeof(float);
+  if (split_len) *split_len = (int32_t)CH;
+  // fp32 partials [B, Hq, S, D+4]: unnormalised O, running max, running sum, pad.
+  if (bytes) *bytes = S == 1 ? 0 : (size_t)B * Hq * S * (D + 4) * sizeof(float);
   return PKB_OK;
 }
 

@@ -19,8 +19,7 @@ struct AttnParams {
   const uint16_t* v;
   void* out;                  // [tokens, Hq, D] bf16 or fp32
   float* lse;                 // [tokens, Hq] or null
-  float* part;                // decode split partials [B, Hq, S, D+2] or null
-  int* counters;              // decode split arrival counters [B, Hkv] (zeroed)
+  float* part;                // decode split partials [B, Hq, S, D+4] or null
   const int32_t* kv_indptr;   // CSR page IDs (bsa, decode)
   const int32_t* kv_indices;
   const int32_t* block_tables;  // row-strided table (prefill)
@@ -37,6 +36,38 @@ struct AttnParams {
   int num_splits, split_len;
   int out_f32;
   float scale_log2;   // softmax scale * log2(e)
+  float out_scale;
+};
+
+// Dedicated single-token decode kernel (GQA group of at most 16 heads): a
+// persistent grid of single-wave workgroups, kDecodeWavesPerCu per CU (one per
+// SIMD measured best: each wave keeps two 32-key groups of loads in flight).
+constexpr int kDecodeWavesPerCu = 4;
+constexpr int kDecodeMaxGroup = 16;
+
+struct DecodeParams {
+  const uint16_t* q;          // [B, Hq, D]
+  const uint16_t* k;
+  const uint16_t* v;
+  void* out;                  // [B, Hq, D]
+  float* lse;                 // [B, Hq] or null
+  float* part;                // [B, Hq, S, D+4] or null (O, m, l, pad)
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* seq_lens;
+  int64_t kv_page_stride, kv_head_stride;
+  int B, Hq, Hkv, G, page_size, window_left;
+  int num_splits, split_len, out_f32;
+  float scale_log2;
+  float out_scale;
+};
+
+struct MergeParams {
+  const float* part;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  int B, Hq, num_splits, split_len, out_f32;
   float out_scale;
 };
 
@@ -58,12 +89,10 @@ struct SageParams {
 
 size_t attn_lds_bytes(int D);
 
-// Decode workspace: arrival counters first, then the partials.
-inline size_t decode_counter_bytes(int B, int Hkv) {
-  return ((size_t)B * Hkv * sizeof(int) + 255) / 256 * 256;
-}
 hipError_t launch_attn(const AttnParams& p, int D, int waves, int mode, dim3 grid,
                        hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int D, int grid, hipStream_t stream);
+hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream);
 hipError_t launch_sage(const SageParams& p, hipStream_t stream);
 
 }  // namespace pkb
