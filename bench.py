@@ -4,13 +4,15 @@
 Headline (the single JSON line's ``value``): batch paged decode, KV-read GB/s --
 B=64 requests, Hq=32 / Hkv=8, D=128, seq_lens ~ U{512..8192}, 16-token pages
 with randomly permuted CSR page IDs, bf16.  One step = one decode launch over
-the whole batch (split-KV with the merge fused into the same kernel).
+the whole batch (the split-KV kernel plus its small merge kernel).
 
 Secondary entries (same JSON line, ``secondary``): long-context block-sparse
 attention (B=4, S=8192, Hq=32/Hkv=8, 16 blocks of 64 per BSR row, causal, 1%
 invalid bits), packed causal prefill (B=8, qlen ~ U{256..2048} + prefix
-~ U{0..2048}), and the tiny block-sparse case -- each as TFLOP/s over the
-admitted (query, key) pairs only (4*D flops per admitted pair and query head).
+~ U{0..2048}), the Sage-style int8/fp8 block-sparse case (B=2, H=16, S=16384,
+64 of 256 blocks per query block) and the tiny block-sparse case -- each as
+TFLOP/s (TOP/s) over the admitted (query, key) pairs only (4*D operations per
+admitted pair and query head).
 
 Timing: inputs are generated (seeded), copied to HBM and planned before the
 timed region; W warm-up launches, then K launches bracketed by device
@@ -238,6 +240,58 @@ def bench_bsa_tiny(steps, warmup, W, P):
             "us_per_launch": round(ms_launch * 1e3, 2)}
 
 
+def sage_admitted_pairs(case):
+    """(query, key) pairs over selected blocks' valid tokens, summed over heads."""
+    B, H, Sq, _ = case.q_int8.shape
+    nqb = -(-Sq // 64)
+    idx = case.q2k_block_index
+    nums = case.q2k_block_nums
+    total = 0
+    for b in range(B):
+        for h in range(H):
+            for r in range(nqb):
+                n = int(nums[b, h, r]) if (nums is not None and not case.uniform_block_count) \
+                    else case.block_sparse_num
+                rows = min(64, Sq - 64 * r)
+                for beta in idx[b, h, r, :n]:
+                    bs = 64
+                    if case.block_sizes is not None:
+                        bsz = case.block_sizes
+                        bs = int(bsz[beta] if bsz.ndim == 1 else (bsz[b, beta] if bsz.ndim == 2
+                                                                   else bsz[b, h, beta]))
+                    total += rows * max(0, min(bs, case.Sk - 64 * int(beta)))
+    return total
+
+
+def bench_sage(steps, warmup, W, P):
+    log("sage: generating inputs")
+    case = W.sage_long()
+    q, k, v = case.q_int8.cuda(), case.k_int8.cuda(), case.v_fp8.cuda()
+    qs, ks, vs = case.q_scale.cuda(), case.k_scale.cuda(), case.v_scale.cuda()
+    idx = dev_i32(case.q2k_block_index)
+    bsz = dev_i32(case.block_sizes)
+    nums = dev_i32(case.q2k_block_nums)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        P.bsa_sage_run(q, k, v, qs, ks, vs, idx, case.block_sparse_num, bsz, nums, None, out=out)
+
+    ms_step, ms_launch = time_launches(step, steps, warmup)
+    pairs = sage_admitted_pairs(case)
+    ops = 4.0 * 128 * pairs
+    tops = ops / (ms_step * 1e-3) / 1e12
+    ach = ops / (ms_launch * 1e-3) / 1e12
+    return {"workload": "Sage block-sparse B=2 H=16 Sq=Sk=16384 D=128 int8 Q/K fp8 V, "
+                        "64 of 256 blocks per query block, last block partial",
+            "metric": "Sage block-sparse TOP/s (admitted pairs, int8 QK + fp8 PV)",
+            "value": round(tops, 2), "unit": "TOP/s", "ms_per_step": round(ms_step, 4),
+            "admitted_pairs": pairs,
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS,
+                         "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4),
+                         "frac_of_bf16_peak": round(ach / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None, "kernel": "sage_kernel"}}
+
+
 def cpu_baseline_decode(case, budget_s=15.0):
     """fp64 oracle on the first requests of the decode batch until ~budget_s."""
     from oracle import attention as A
@@ -270,7 +324,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["decode", "bsa", "prefill", "tiny"], default=None,
+    ap.add_argument("--only", choices=["decode", "bsa", "prefill", "tiny", "sage"], default=None,
                     help="run one workload only (for profiling)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -287,7 +341,8 @@ def main(argv=None):
     if a.only and a.only != "decode":
         fn = {"bsa": lambda: bench_bsa_long(a.steps, a.warmup, W, P),
               "prefill": lambda: bench_prefill(a.steps, a.warmup, W, P),
-              "tiny": lambda: bench_bsa_tiny(a.steps, a.warmup, W, P)}[a.only]
+              "tiny": lambda: bench_bsa_tiny(a.steps, a.warmup, W, P),
+              "sage": lambda: bench_sage(a.steps, a.warmup, W, P)}[a.only]
         print(json.dumps(fn()), flush=True)
         return 0
 
@@ -299,6 +354,7 @@ def main(argv=None):
                    lambda: bench_prefill(a.steps, a.warmup, W, P),
                    lambda: bench_prefill(a.steps, a.warmup, W, P, window_left=1024),
                    lambda: bench_prefill(a.steps, a.warmup, W, P, D=256),
+                   lambda: bench_sage(a.steps, a.warmup, W, P),
                    lambda: bench_bsa_tiny(a.steps, a.warmup, W, P)):
             r = fn()
             log(f"{r['workload']}: {r['value']} {r['unit']}")
