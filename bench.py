@@ -185,7 +185,8 @@ def bench_bsa_long(steps, warmup, W, P):
             "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel": "attn_fwd_kernel<128,4,bsa>"}}
+                         "traffic": None,
+                         "kernel": "attn_fwd_kernel<128,%d,bsa>" % wr.plan.waves}}
 
 
 def bench_prefill(steps, warmup, W, P, D=128, window_left=-1):
@@ -214,7 +215,8 @@ def bench_prefill(steps, warmup, W, P, D=128, window_left=-1):
             "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel": "attn_fwd_kernel<%d,4,prefill>" % D}}
+                         "traffic": None,
+                         "kernel": "attn_fwd_kernel<%d,%d,prefill>" % (D, wr.plan.waves)}}
 
 
 def bench_bsa_tiny(steps, warmup, W, P):

@@ -99,7 +99,7 @@ int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
   if (!plan) return PKB_ERR_ARG;
   const prefill_static_args& a = plan->a;
   if (a.B < 1 || a.Hkv < 1 || a.Hq % a.Hkv || (a.D != 128 && a.D != 256) ||
-      plan->waves != 4 || plan->group != a.Hq / a.Hkv)
+      plan->waves != (a.D == 128 ? 8 : 4) || plan->group != a.Hq / a.Hkv)
     return PKB_ERR_ARG;
   if (a.mask_type != PKB_MASK_DENSE && a.mask_type != PKB_MASK_CAUSAL) return PKB_ERR_ARG;
   if (a.window_left < -1 || (a.window_left >= 0 && a.mask_type != PKB_MASK_CAUSAL))
@@ -140,7 +140,8 @@ int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
   p.scale_log2 = scale_or_default(sm_scale, a.D) * 1.4426950408889634f;
   p.out_scale = output_scale;
   dim3 grid(plan->grid_x, plan->grid_y, 1);
-  return hip_status(pkb::launch_attn(p, a.D, 4, pkb::kModePrefill, grid, (hipStream_t)stream));
+  return hip_status(pkb::launch_attn(p, a.D, plan->waves, pkb::kModePrefill, grid,
+                                     (hipStream_t)stream));
 }
 
 int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv_page_stride,

@@ -12,70 +12,119 @@
 // Work decomposition.  One workgroup = (request, KV head, tile of packed query
 // rows).  Query heads of one GQA group are packed into the row dimension
 // (row = token * group + head_in_group), so a KV tile loaded once serves every
-// head of the group.  Each wavefront owns 32 packed rows.
+// head of the group.  Each wavefront owns 32 packed rows; up to 8 waves share
+// one KV tile.
 //
-// Per 64-key tile:
-//   * the tile is 8 chunks of 8 logical tokens; an 8-token run never crosses a
-//     page (page and block sizes are multiples of 8), so each chunk is one
-//     contiguous [8, D] slab of the HND pool, fetched with 16-byte loads;
-//   * K goes to LDS row-major [key][D] (rows padded by 16 B so the MFMA reads of
-//     32 consecutive keys hit distinct banks);
-//   * V goes to LDS transposed, [D][key], with the keys of every 16-key group
-//     stored in the order 0-3, 8-11, 4-7, 12-15 (explained at the PV step);
+// KV tiles are 64 keys = 8 chunks of 8 logical tokens.  An 8-token run never
+// crosses a page (page and block sizes are multiples of 8), so each chunk is one
+// contiguous [8, D] slab of the HND pool.  Tiles go HBM -> LDS through
+// direct-to-LDS loads (global_load_lds_dwordx4: 1 KB per wave instruction, no
+// registers) into a ring of NSTAGE buffers, NSTAGE-1 tiles ahead of use, with
+// one workgroup barrier per tile.  Rows are stored unpadded with their 16-byte
+// pieces permuted per row: K piece l sits at l ^ (key & 15), so the A-operand
+// reads of 16 consecutive keys hit distinct banks; the V permutation (v_swz)
+// spreads the four 16-lane groups of a transpose read over all 64 banks.
+//
+// A tile is described by a 64-bit mask of the keys that can be admitted (live,
+// valid, inside the workgroup's causal/window band) and the first token of each
+// chunk.  Where the visited keys are contiguous (prefill, decode, and sparse
+// blocks of 64 or more keys) that is one start token and the mask comes from a
+// few scalar operations; only the chunk a wave copies needs its page looked up.
+// Dead chunks copy the tile's first live chunk and rows at or past the live
+// length re-read their chunk's first row, so LDS never holds non-finite data.
+//
+// Per tile and wave:
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (M = keys, N = query rows,
-//     K = head dim): every lane then holds 16 keys of ONE query row, so the row
-//     max needs one exchange between the two half-waves and the row sum none
-//     until the epilogue;
-//   * online softmax in base 2 (the scale is folded with log2 e);
-//   * O^T += V^T P^T, again 32x32x16 MFMAs.  The B operand P^T is taken straight
-//     from the S^T accumulator: lane (row n, half h) holds keys {4h..4h+3,
-//     8+4h..8+4h+3} of every 16-key step, which is exactly what the permuted V^T
-//     rows provide at positions 8h..8h+7, so no data moves between the two
-//     products.
-// The next tile's page translation and global loads are issued before the
-// current tile's MFMAs so HBM traffic overlaps compute.
+//     K = head dim): every lane holds 16 keys of ONE query row per 32 keys, so
+//     the row max needs one exchange between the two half-waves;
+//   * masks are applied only to tiles that need them (an invalid or cut key,
+//     the causal diagonal, the window edge);
+//   * online softmax in base 2: exp2(s * scale * log2 e - m) as one FMA and one
+//     exp; the running output is rescaled only when some row max moved;
+//   * O^T += V^T P^T: the V^T operand comes from ds_read_b64_tr_b16, which
+//     returns a 4-key x 16-dim block of the row-major V tile column-wise; lane
+//     half h then holds keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key step --
+//     exactly the keys its S^T accumulator holds, so P^T feeds the MFMA as is.
 #include "device_common.h"
 #include "pkb_internal.h"
 
 namespace pkb {
 
-template <int D>
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef float f32x2e __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2e __attribute__((ext_vector_type(2)));
+
+template <int D, int NW>
 struct AttnLayout {
-  static constexpr int KT = kKvTile;          // keys per tile
-  static constexpr int PPK = D / 8;           // 16-byte pieces per key row
-  static constexpr int KROW = D * 2 + 16;     // bytes per K row in LDS
-  static constexpr int VROW = KT * 2 + 16;    // bytes per V^T row in LDS
-  static constexpr int K_BYTES = KT * KROW;
-  static constexpr int V_BYTES = D * VROW;
-  static constexpr int LDS = K_BYTES + V_BYTES;
+  static constexpr int KT = kKvTile;             // keys per tile
+  static constexpr int ROWB = D * 2;             // bytes per K / V row
+  static constexpr int TILE_B = KT * ROWB;       // bytes of a K (or V) tile
+  static constexpr int NSTAGE = (D == 128 && NW == 8) ? 3 : 2;
+  static constexpr int STAGE_B = 2 * TILE_B;
+  static constexpr int LDS = NSTAGE * STAGE_B;
+  static constexpr int INSTR = TILE_B / 1024;    // 1 KB DMA instructions per K (or V) tile
+  static constexpr int KPI = 1024 / ROWB;        // key rows per DMA instruction
+  static constexpr int LPK = 64 / KPI;           // lanes per key row in one instruction
+  static constexpr int IPW = INSTR / NW;         // K (and V) instructions per wave per tile
 };
 
-size_t attn_lds_bytes(int D) {
-  return D == 128 ? AttnLayout<128>::LDS : AttnLayout<256>::LDS;
+// Physical 16-byte piece of logical piece lp in V row `key`, and its inverse.
+// The XOR with 2*(key & 3) separates the four rows of one transpose read; the
+// bit-3 flip by (bit 1 of lp) ^ (bit 2 of key) moves the 16-lane groups that
+// read other dims or other rows of the same 16-key step to the other 32 banks.
+__device__ __forceinline__ int v_swz(int key, int lp) {
+  const int x = lp ^ (2 * (key & 3));
+  return x ^ (8 * (((lp >> 1) & 1) ^ ((key >> 2) & 1)));
+}
+__device__ __forceinline__ int v_unswz(int key, int pp) {
+  const int x = pp ^ (2 * (key & 3));
+  return x ^ (8 * (((x >> 1) & 1) ^ ((key >> 2) & 1)));
 }
 
-// Position of key k (0..63) inside a permuted V^T row.
-__device__ __forceinline__ int vt_pos(int k) {
-  const int b4 = (k >> 2) & 3;
-  const int nb4 = (b4 == 1) ? 2 : (b4 == 2 ? 1 : b4);
-  return (k & ~15) + nb4 * 4 + (k & 3);
+// Two floats -> packed bf16 pair (round to nearest even) in one instruction.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const f32x2e v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2e));
 }
 
-template <int D, int NW, int MODE>
+// Waits until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16 bytes per lane from global src to LDS address lds_addr + 16 * lane
+// (global_load_lds_dwordx4; the LDS base is taken from M0, which needs one wait
+// state after the SALU write).  Written as inline assembly so the compiler does
+// not treat every later LDS read as depending on every copy in flight: the
+// kernel orders copies and reads itself with s_waitcnt vmcnt and barriers.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
+// One KV tile, wave-uniform.
+struct TileMeta {
+  uint64_t M;       // bit k: key k may be admitted (live, valid, inside [k_lo, k_hi))
+  int t0;           // first token (contiguous tiles)
+  int t_first;      // first token of the first chunk with an admissible key
+  int tmin, tmax;   // token range of the tile's chunks with admissible keys
+  int ts[8];        // first token of each chunk (tiles of small sparse blocks)
+};
+
+template <int D, int NW, int MODE, bool F32, bool CONTIG>
 __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
-  using Lay = AttnLayout<D>;
-  constexpr int NT = NW * 64;
+  using Lay = AttnLayout<D, NW>;
   constexpr int TILE_M = 32 * NW;
-  constexpr int PPK = Lay::PPK;
   constexpr int NKS = D / 16;           // S^T k-steps over the head dim
   constexpr int NDB = D / 32;           // 32-row blocks of O^T
-  constexpr int K_PASSES = (Lay::KT * PPK) / NT;
-  constexpr int V_PASSES = (16 * PPK) / NT;
-  static_assert(K_PASSES >= 1 && V_PASSES >= 1, "tile too small for the workgroup");
+  constexpr int IPW = Lay::IPW;
+  constexpr int PD = Lay::NSTAGE - 1;   // tiles in flight ahead of the one computed
+  static_assert(Lay::INSTR % NW == 0, "tile instructions must split evenly over waves");
 
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* sK = smem;
-  unsigned char* sV = smem + Lay::K_BYTES;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,16 +191,138 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
     k_hi = min(k_hi, (split + 1) * p.split_len);
   }
 
-  int n_vchunks, lo8 = 0;
+  // visited KV: contiguous modes walk [lo8, k_hi) in 64-token tiles; sparse
+  // rows walk their selected blocks in order, 8-token chunks packed 8 per tile
+  int n_tiles, lo8 = 0;
   if (MODE == kModeBsa) {
-    n_vchunks = n_sel * (p.kvbs >> 3);
+    n_tiles = CONTIG ? n_sel * (p.kvbs >> 6) : (n_sel * (p.kvbs >> 3) + 7) >> 3;
   } else {
     lo8 = k_lo & ~7;
-    n_vchunks = (k_hi > k_lo) ? (k_hi - lo8 + 7) >> 3 : 0;
+    n_tiles = (k_hi > k_lo) ? (k_hi - lo8 + 63) >> 6 : 0;
   }
-  const int n_tiles = (n_vchunks + 7) >> 3;
 
-  // ---------------- Q fragments (B operand of S^T) ----------------
+  // ---------------- tile metadata (scalar; identical in every wave) ----------------
+  const int64_t head_off = (int64_t)kvh * p.kv_head_stride;
+  const int32_t* ids = MODE == kModePrefill ? p.block_tables + (int64_t)b * p.bt_stride
+                                            : p.kv_indices + p.kv_indptr[b];
+  const int ps_sh = __builtin_ctz(p.page_size | 0x40000000);
+  const bool ps_pow2 = (p.page_size & (p.page_size - 1)) == 0;
+  const int blk_tiles = p.kvbs >> 6;                 // tiles per sparse block (>= 64 keys)
+  const int bt_sh = __builtin_ctz(blk_tiles | 0x40000000);
+  const bool bt_pow2 = (blk_tiles & (blk_tiles - 1)) == 0;
+  const int cpb_sh = __builtin_ctz((p.kvbs >> 3) | 0x40000000);   // chunks per small block (1, 2, 4)
+
+  // admissible bits of the 8 keys from token t (a multiple of 8)
+  auto chunk_bits = [&](int t) -> uint32_t {
+    const int lo_cut = min(max(k_lo - t, 0), 8);
+    const int hi_cut = min(max(k_hi - t, 0), 8);
+    uint32_t bits = ((1u << hi_cut) - 1u) & ~((1u << lo_cut) - 1u);
+    if (MODE == kModeBsa && p.valid_bits && bits)
+      bits &= ld_const(p.valid_bits, (int64_t)b * p.valid_words + (t >> 5)) >> (t & 31);
+    return bits & 0xFFu;
+  };
+  // first token of chunk v of a row's small-block walk
+  auto small_chunk_token = [&](int v) -> int {
+    const int qq = v >> cpb_sh;
+    return ld_const(p.block_indices, bip_lo + qq) * p.kvbs + (v - (qq << cpb_sh)) * 8;
+  };
+  // element offset of token t's row in the K (V) pool
+  auto token_src = [&](int t) -> int64_t {
+    const int pi = ps_pow2 ? (t >> ps_sh) : t / p.page_size;
+    const int slot = t - pi * p.page_size;
+    return (int64_t)ld_const(ids, pi) * p.kv_page_stride + head_off + (int64_t)slot * D;
+  };
+
+  auto tile_meta = [&](int j) -> TileMeta {
+    TileMeta tm;
+    if (CONTIG) {
+      int t0;
+      if (MODE == kModeBsa) {
+        const int qq = bt_pow2 ? (j >> bt_sh) : j / blk_tiles;
+        t0 = ld_const(p.block_indices, bip_lo + qq) * p.kvbs + (j - qq * blk_tiles) * 64;
+      } else {
+        t0 = lo8 + 64 * j;
+      }
+      const int lo = min(max(k_lo - t0, 0), 64);
+      const int hi = min(max(k_hi - t0, 0), 64);
+      uint64_t M = (hi >= 64 ? ~0ull : ((1ull << hi) - 1ull)) & ~(lo >= 64 ? ~0ull : ((1ull << lo) - 1ull));
+      if (MODE == kModeBsa && p.valid_bits && M) {
+        // t0 is a multiple of 64 here; the second word exists when t0 + 32 < L
+        const int64_t w = (int64_t)b * p.valid_words + (t0 >> 5);
+        uint64_t bits = ld_const(p.valid_bits, w);
+        if (t0 + 32 < L) bits |= (uint64_t)ld_const(p.valid_bits, w + 1) << 32;
+        M &= bits;
+      }
+      tm.M = M;
+      tm.t0 = t0;
+      const int c_first = M ? (__builtin_ctzll(M) >> 3) : 0;
+      const int c_last = M ? ((63 - __builtin_clzll(M)) >> 3) : 0;
+      tm.t_first = t0 + 8 * c_first;
+      tm.tmin = t0 + 8 * c_first;
+      tm.tmax = t0 + 8 * c_last + 7;
+    } else {
+      uint64_t M = 0;
+      int t_first = -1, tmin = 0x7fffffff, tmax = -1;
+      const int nch = n_sel << cpb_sh;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int v = j * 8 + c;
+        tm.ts[c] = 0;
+        if (v < nch) {
+          const int t = small_chunk_token(v);
+          tm.ts[c] = t;
+          const uint32_t bw = chunk_bits(t);
+          M |= (uint64_t)bw << (8 * c);
+          if (bw) {
+            if (t_first < 0) t_first = t;
+            tmin = min(tmin, t);
+            tmax = max(tmax, t + 7);
+          }
+        }
+      }
+      tm.M = M;
+      tm.t0 = 0;
+      tm.t_first = t_first;
+      tm.tmin = tmin;
+      tm.tmax = tmax;
+    }
+    return tm;
+  };
+
+  // This wave's share of tile j's copies into stage st.  Lane l of K (V)
+  // instruction i writes LDS bytes i*1024 + 16l: row i*KPI + l/LPK, physical
+  // piece l%LPK, so it fetches the logical piece stored there.
+  auto issue_tile = [&](const TileMeta& tm, int j, int st) {
+    const uint32_t kst = lds_base + st * Lay::STAGE_B;
+    const uint32_t vst = kst + Lay::TILE_B;
+#pragma unroll
+    for (int ii = 0; ii < IPW; ++ii) {
+      const int i = wave * IPW + ii;
+      const int c = (i * Lay::KPI) >> 3;
+      int t;
+      if ((tm.M >> (8 * c)) & 0xFFu) t = CONTIG ? tm.t0 + 8 * c : small_chunk_token(j * 8 + c);
+      else t = tm.t_first;
+      const int64_t src = token_src(t);
+      const int key = i * Lay::KPI + lane / Lay::LPK;
+      const int r = key & 7;
+      const int rr = (t + r < L) ? r : 0;
+      const int pp = lane % Lay::LPK;
+      lds_dma16(p.k + src + rr * D + (pp ^ (key & 15)) * 8, kst + i * 1024);
+      lds_dma16(p.v + src + rr * D + v_unswz(key, pp) * 8, vst + i * 1024);
+    }
+  };
+
+  // ---------------- prologue: first tiles in flight, then Q ----------------
+  TileMeta tmr[PD + 1];   // tmr[k] = tile j + k
+#pragma unroll
+  for (int k = 0; k < PD; ++k) {
+    tmr[k].M = 0;
+    if (k < n_tiles) {
+      tmr[k] = tile_meta(k);
+      if (tmr[k].M) issue_tile(tmr[k], k, k);
+    }
+  }
+
   bf16x8 qf[NKS];
   {
     const uint16_t* qrow = p.q + ((int64_t)(tok_base + my_i) * p.Hq + my_hq) * D + 8 * hh;
@@ -162,105 +333,28 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
       qf[s] = as_bf16x8(x);
     }
   }
+  // Q and every copy issued so far complete here, so no load issued before the
+  // tile loop is pending inside it.
+  wait_vmcnt<0>();
 
-  // ---------------- chunk translation (lanes 0..7 of every wave) ----------------
-  // ts: first logical token of the chunk, or -1 when the chunk is dead;
-  // off: element offset of the chunk's [8, D] slab; bw: 8 live bits (validity
-  // bit, inside [k_lo, k_hi) and < L), LSB = first token.
-  auto chunk_info = [&](int j, int& ts, int64_t& off, int& bw) {
-    const int c = lane & 7;
-    const int v = j * 8 + c;
-    ts = -1; off = 0; bw = 0;
-    if (lane < 8 && v < n_vchunks) {
-      int64_t t;
-      if (MODE == kModeBsa) {
-        const int cpb = p.kvbs >> 3;
-        const int q = v / cpb;
-        t = (int64_t)p.block_indices[bip_lo + q] * p.kvbs + (int64_t)(v - q * cpb) * 8;
-      } else {
-        t = lo8 + (int64_t)v * 8;
-      }
-      if (t < k_hi && t + 8 > k_lo) {
-        const int ti = (int)t;
-        const int pi = ti / p.page_size;
-        const int slot = ti - pi * p.page_size;
-        int page;
-        if (MODE == kModePrefill) page = p.block_tables[(int64_t)b * p.bt_stride + pi];
-        else page = p.kv_indices[p.kv_indptr[b] + pi];
-        off = (int64_t)page * p.kv_page_stride + (int64_t)kvh * p.kv_head_stride +
-              (int64_t)slot * D;
-        ts = ti;
-        uint32_t bits = 0xFFu;
-        if (p.valid_bits) bits = (p.valid_bits[(int64_t)b * p.valid_words + (ti >> 5)] >> (ti & 31)) & 0xFFu;
-        const int lo_cut = max(k_lo - ti, 0);                 // tokens below k_lo
-        const int hi_cut = min(max(k_hi - ti, 0), 8);         // tokens >= k_hi dead
-        uint32_t range = ((1u << hi_cut) - 1u) & ~((1u << lo_cut) - 1u);
-        bw = (int)(bits & range);
-      }
-    }
-  };
-
-  // ---------------- global -> register staging ----------------
-  u32x4 kreg[K_PASSES];
-  u32x4 vreg[V_PASSES][4];
-  const int kg = tid & 15;                 // V: 4-key group handled by this lane
-  auto load_tile = [&](int ts_v, int64_t off_v) {
-    // K: pass i covers keys tid/PPK + (NT/PPK)*i, piece tid%PPK (wave-uniform chunk)
+  // ---------------- per-lane LDS offsets ----------------
+  // K (A operand of S^T): lane (ql, hh) reads key ql (+32 for the second block),
+  // logical piece 2s + hh; pieces 16.. of a 256-dim row add 256 bytes.
+  int koff[8];
 #pragma unroll
-    for (int i = 0; i < K_PASSES; ++i) {
-      const int key = tid / PPK + (NT / PPK) * i;
-      const int c = wave_uniform(key >> 3);
-      const int tsc = readlane_i32(ts_v, c);
-      const int64_t offc = readlane_i64(off_v, c);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (tsc >= 0) x = ld_global_16(p.k + offc + (key & 7) * D + (tid % PPK) * 8);
-      kreg[i] = x;
-    }
-    // V: lane handles keys 4kg..4kg+3 and d-piece (tid>>4) + (NT/16)*i
-    const int c = kg >> 1;
-    const int tsc = shfl_i32(ts_v, c);
-    const int64_t offc = shfl_i64(off_v, c);
+  for (int s = 0; s < 8; ++s) koff[s] = ql * Lay::ROWB + (((2 * s + hh) ^ (ql & 15)) * 16);
+  // V (transpose reads): 16-lane group q16 covers dims 16*(q16&1) of a 32-dim
+  // block for key half hq = q16>>1; lane 4r + c of the group reads key row
+  // k0 + r, dims +4c..+4c+3, with k0 = 16s + 4hq (+8 for the second read).
+  const int q16 = lane >> 4, li = lane & 15;
+  const int v_r = li >> 2, v_c = li & 3;
+  const int v_hq = q16 >> 1, v_dsub = q16 & 1;
+  int voff[4];
 #pragma unroll
-    for (int i = 0; i < V_PASSES; ++i) {
-      const int dp = (tid >> 4) + (NT / 16) * i;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (tsc >= 0) x = ld_global_16(p.v + offc + (4 * (kg & 1) + e) * D + dp * 8);
-        vreg[i][e] = x;
-      }
-    }
-  };
-
-  auto store_tile = [&](int bw_v) {
-#pragma unroll
-    for (int i = 0; i < K_PASSES; ++i) {
-      const int key = tid / PPK + (NT / PPK) * i;
-      *(u32x4*)(sK + key * Lay::KROW + (tid % PPK) * 16) = kreg[i];
-    }
-    // zero V rows of dead keys (never multiply 0 by non-finite data)
-    const int bwc = shfl_i32(bw_v, kg >> 1) >> (4 * (kg & 1));
-    const int pos = vt_pos(4 * kg);
-#pragma unroll
-    for (int i = 0; i < V_PASSES; ++i) {
-      const int dp = (tid >> 4) + (NT / 16) * i;
-      u32x4 r[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool live = (bwc >> e) & 1;
-        r[e] = live ? vreg[i][e] : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const uint32_t sel = (e8 & 1) ? 0x07060302u : 0x05040100u;
-        const int w = e8 >> 1;
-        u32x2 d2;
-        d2[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
-        d2[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);
-        *(u32x2*)(sV + (dp * 8 + e8) * Lay::VROW + pos * 2) = d2;
-      }
-    }
-  };
+  for (int d = 0; d < 4; ++d) {
+    const int key = 4 * v_hq + v_r;
+    voff[d] = key * Lay::ROWB + v_swz(key, 4 * d + 2 * v_dsub + (v_c >> 1)) * 16 + 8 * (v_c & 1);
+  }
 
   // ---------------- accumulators ----------------
   f32x16 oacc[NDB];
@@ -268,75 +362,66 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
   for (int d = 0; d < NDB; ++d)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;   // running max of scale*log2(e)*s
   float l_run = 0.f;
   const float sl2 = p.scale_log2;
   const int wl = p.window_left;
-  const bool precise = p.out_f32 != 0;   // fp32 output requested
-
-  int cur_ts = -1, cur_bw = 0;
-  int64_t cur_off = 0;
-  if (n_tiles > 0) {
-    chunk_info(0, cur_ts, cur_off, cur_bw);
-    load_tile(cur_ts, cur_off);
-  }
+  const int myp4 = my_p - 4 * hh;        // causal: lane admits tile token tk + 4hh iff tk <= myp4
+  const int myw4 = my_p - wl - 4 * hh;   // window: ... iff tk >= myw4
 
   for (int j = 0; j < n_tiles; ++j) {
-    int nxt_ts = -1, nxt_bw = 0;
-    int64_t nxt_off = 0;
-    const bool has_next = (j + 1) < n_tiles;
-    if (has_next) chunk_info(j + 1, nxt_ts, nxt_off, nxt_bw);
-
-    __syncthreads();                  // previous tile's LDS reads are done
-    store_tile(cur_bw);
-    __syncthreads();
-
-    int tsu[8], bwu[8];
-    int any_live = 0, all_full = 1, ts_min = 0x7fffffff, ts_max = -1;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      tsu[c] = readlane_i32(cur_ts, c);
-      bwu[c] = readlane_i32(cur_bw, c);
-      any_live |= bwu[c];
-      all_full &= (bwu[c] == 0xFF);
-      if (tsu[c] >= 0) { ts_min = min(ts_min, tsu[c]); ts_max = max(ts_max, tsu[c]); }
+    const int st = j % Lay::NSTAGE;
+    // this wave's copies of tile j have landed (later tiles may still fly)
+    if (PD == 2 && j + 1 < n_tiles && tmr[1].M) wait_vmcnt<2 * IPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();     // all of tile j is in LDS; every wave is done with tile j-1
+    tmr[PD].M = 0;
+    if (j + PD < n_tiles) {
+      tmr[PD] = tile_meta(j + PD);
+      if (tmr[PD].M) issue_tile(tmr[PD], j + PD, (j + PD) % Lay::NSTAGE);   // tile j-1's stage
     }
+    const TileMeta& tm = tmr[0];
 
-    if (has_next) load_tile(nxt_ts, nxt_off);
-
-    if (wave_rows && any_live) {
+    if (wave_rows && tm.M) {
+      const unsigned char* sK = smem + st * Lay::STAGE_B;
+      const unsigned char* sV = sK + Lay::TILE_B;
       // ---- S^T = K Q^T for two 32-key blocks ----
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-        const unsigned char* kr = sK + (32 * kb + ql) * Lay::KROW + 16 * hh;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          const bf16x8 a = *(const bf16x8*)(kr + 32 * s);
+          const bf16x8 a = *(const bf16x8*)(sK + koff[s & 7] + (s >> 3) * 256 + kb * 32 * Lay::ROWB);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
         }
       }
-      // ---- scale + mask ----
-      const bool fast = all_full && (!p.causal || ts_max + 7 <= wp_lo) &&
-                        (wl < 0 || ts_min >= wp_hi - wl);
+      // ---- masks (element i of block kb is key 32kb + 8(i>>2) + 4hh + (i&3)) ----
+      auto chunk_t = [&](int c) { return CONTIG ? tm.t0 + 8 * c : tm.ts[c]; };
+      if (tm.M != ~0ull) {
+        const uint64_t Mh = hh ? (tm.M >> 4) : tm.M;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float s = sacc[kb][i] * sl2;
-          if (!fast) {
-            const int c = 4 * kb + (i >> 2);
-            const int e = 4 * hh + (i & 3);
-            const int tok = tsu[c] + e;
-            bool ok = (bwu[c] >> e) & 1;
-            if (p.causal) ok = ok && tok <= my_p;
-            if (wl >= 0) ok = ok && tok >= my_p - wl;
-            s = ok ? s : -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int pos = 32 * kb + 8 * (i >> 2) + (i & 3);
+            if (!((Mh >> pos) & 1)) sacc[kb][i] = -INFINITY;
           }
-          sacc[kb][i] = s;
-        }
+      }
+      if (p.causal && tm.tmax > wp_lo) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (chunk_t(4 * kb + (i >> 2)) + (i & 3) > myp4) sacc[kb][i] = -INFINITY;
+      }
+      if (wl >= 0 && tm.tmin < wp_hi - wl) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (chunk_t(4 * kb + (i >> 2)) + (i & 3) < myw4) sacc[kb][i] = -INFINITY;
       }
       // ---- online softmax ----
       float mx = -INFINITY;
@@ -345,24 +430,27 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
       mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = fmaxf(m_run, mx * sl2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(sacc[kb][i] - m_use);
+          const float e = fast_exp2(__builtin_fmaf(sacc[kb][i], sl2, -m_use));
           sacc[kb][i] = e;
           psum += e;
         }
-      l_run = l_run * alpha + psum;
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {   // some row max moved
+        const float alpha = fast_exp2(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      }
+      l_run += psum;
       m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
 
       // ---- O^T += V^T P^T ----
       bf16x8 pb[4];
@@ -371,46 +459,47 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
         u32x4 w;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          w[t] = pack_bf16x2(sacc[s >> 1][8 * (s & 1) + 2 * t], sacc[s >> 1][8 * (s & 1) + 2 * t + 1]);
+          w[t] = cvt_pk_bf16(sacc[s >> 1][8 * (s & 1) + 2 * t], sacc[s >> 1][8 * (s & 1) + 2 * t + 1]);
         pb[s] = as_bf16x8(w);
       }
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        const unsigned char* vr = sV + (32 * d + ql) * Lay::VROW + 16 * hh;
+        bf16x8 va[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = *(const bf16x8*)(vr + 32 * s);
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], oacc[d], 0, 0, 0);
-        }
-      }
-      if (precise) {
-        // fp32 output: add P - bf16(P) as a second bf16 operand, so the
-        // probabilities enter the PV product with ~16 significant bits.
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 hi = __builtin_bit_cast(u32x4, pb[s]);
+          const unsigned char* a = sV + voff[d & 3] + (d >> 2) * 256 + 16 * s * Lay::ROWB;
+          const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(a));
+          const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(a + 8 * Lay::ROWB));
+          const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
           u32x4 w;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float p0 = sacc[s >> 1][8 * (s & 1) + 2 * t];
-            const float p1 = sacc[s >> 1][8 * (s & 1) + 2 * t + 1];
-            w[t] = pack_bf16x2(p0 - __uint_as_float(hi[t] << 16),
-                               p1 - __uint_as_float(hi[t] & 0xFFFF0000u));
-          }
-          pb[s] = as_bf16x8(w);
+          w[0] = y0[0]; w[1] = y0[1]; w[2] = y1[0]; w[3] = y1[1];
+          va[s] = as_bf16x8(w);
         }
 #pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          const unsigned char* vr = sV + (32 * d + ql) * Lay::VROW + 16 * hh;
+        for (int s = 0; s < 4; ++s)
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], pb[s], oacc[d], 0, 0, 0);
+        if (F32) {
+          // fp32 output: add P - bf16(P) as a second bf16 operand (~16-bit P)
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const bf16x8 a = *(const bf16x8*)(vr + 32 * s);
-            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], oacc[d], 0, 0, 0);
+            const u32x4 hi = __builtin_bit_cast(u32x4, pb[s]);
+            u32x4 w;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float p0 = sacc[s >> 1][8 * (s & 1) + 2 * t];
+              const float p1 = sacc[s >> 1][8 * (s & 1) + 2 * t + 1];
+              w[t] = cvt_pk_bf16(p0 - __uint_as_float(hi[t] << 16),
+                                 p1 - __uint_as_float(hi[t] & 0xFFFF0000u));
+            }
+            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], as_bf16x8(w), oacc[d], 0, 0, 0);
           }
         }
       }
     }
-    cur_ts = nxt_ts; cur_off = nxt_off; cur_bw = nxt_bw;
+#pragma unroll
+    for (int k = 0; k < PD; ++k) tmr[k] = tmr[k + 1];
   }
 
   // ---------------- epilogue ----------------
@@ -441,7 +530,7 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_tot;
   const int64_t orow = ((int64_t)(tok_base + my_i) * p.Hq + my_hq);
-  if (p.out_f32) {
+  if (F32) {
     float* o = (float*)p.out + orow * D;
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
@@ -471,8 +560,14 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
 
 template <int D, int NW, int MODE>
 static hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t st) {
-  const size_t lds = AttnLayout<D>::LDS;
-  const void* kern = (const void*)attn_fwd_kernel<D, NW, MODE>;
+  const size_t lds = AttnLayout<D, NW>::LDS;
+  const void* kern = p.out_f32 ? (const void*)attn_fwd_kernel<D, NW, MODE, true, true>
+                               : (const void*)attn_fwd_kernel<D, NW, MODE, false, true>;
+  if constexpr (MODE == kModeBsa) {
+    if (p.kvbs % 64 != 0)   // sparse blocks of 8, 16 or 32 keys: several per tile
+      kern = p.out_f32 ? (const void*)attn_fwd_kernel<D, NW, MODE, true, false>
+                       : (const void*)attn_fwd_kernel<D, NW, MODE, false, false>;
+  }
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -488,8 +583,10 @@ static hipError_t launch_d(const AttnParams& p, int waves, int mode, dim3 grid, 
     if (waves == 1) return launch_one<D, 1, kModeBsa>(p, grid, st);
     if (waves == 2) return launch_one<D, 2, kModeBsa>(p, grid, st);
     if (waves == 4) return launch_one<D, 4, kModeBsa>(p, grid, st);
+    if (D == 128 && waves == 8) return launch_one<128, 8, kModeBsa>(p, grid, st);
   } else if (mode == kModePrefill) {
-    if (waves == 4) return launch_one<D, 4, kModePrefill>(p, grid, st);
+    if (D == 256 && waves == 4) return launch_one<256, 4, kModePrefill>(p, grid, st);
+    if (D == 128 && waves == 8) return launch_one<128, 8, kModePrefill>(p, grid, st);
   } else if (mode == kModeDecode) {
     if (waves == 4) return launch_one<D, 4, kModeDecode>(p, grid, st);
   }

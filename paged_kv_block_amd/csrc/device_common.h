@@ -76,4 +76,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ u32x4 ld_global_16(const void* p) { return *(const u32x4*)p; }
 
+// Load of kernel-read-only data through the constant address space: with a
+// wave-uniform index this is a scalar load, whatever stores or direct-to-LDS
+// copies the kernel issues around it.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 }  // namespace pkb

@@ -87,8 +87,6 @@ struct SageParams {
   float scale_log2;
 };
 
-size_t attn_lds_bytes(int D);
-
 hipError_t launch_attn(const AttnParams& p, int D, int waves, int mode, dim3 grid,
                        hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int D, int grid, hipStream_t stream);
