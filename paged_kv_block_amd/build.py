@@ -28,7 +28,8 @@ HIP_SOURCES = ["attn_fwd.hip", "decode_fwd.hip", "sage_fwd.hip", "api.cpp"]
 # Per-source extra device flags.  The decode kernel fits in the 256 architectural
 # VGPRs, so its MFMA operands and accumulators are kept there: VALU work on the
 # accumulators (rescale, epilogue) then needs no AGPR <-> VGPR copies.
-SOURCE_FLAGS = {"decode_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+SOURCE_FLAGS = {"decode_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 CPP_SOURCES = ["host.cpp"]
 
 

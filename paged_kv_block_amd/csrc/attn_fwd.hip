@@ -12,14 +12,14 @@
 // Work decomposition.  One workgroup = (request, KV head, tile of packed query
 // rows).  Query heads of one GQA group are packed into the row dimension
 // (row = token * group + head_in_group), so a KV tile loaded once serves every
-// head of the group.  Each wavefront owns 32 packed rows; up to 8 waves share
-// one KV tile.
+// head of the group.  Each wavefront owns 32 packed rows; up to 8 waves (two
+// per SIMD) share one KV tile.
 //
 // KV tiles are 64 keys = 8 chunks of 8 logical tokens.  An 8-token run never
 // crosses a page (page and block sizes are multiples of 8), so each chunk is one
 // contiguous [8, D] slab of the HND pool.  Tiles go HBM -> LDS through
 // direct-to-LDS loads (global_load_lds_dwordx4: 1 KB per wave instruction, no
-// registers) into a ring of NSTAGE buffers, NSTAGE-1 tiles ahead of use, with
+// registers) into a K ring and a V ring, one or two tiles ahead of use, with
 // one workgroup barrier per tile.  Rows are stored unpadded with their 16-byte
 // pieces permuted per row: K piece l sits at l ^ (key & 15), so the A-operand
 // reads of 16 consecutive keys hit distinct banks; the V permutation (v_swz)
@@ -29,18 +29,20 @@
 // valid, inside the workgroup's causal/window band) and the first token of each
 // chunk.  Where the visited keys are contiguous (prefill, decode, and sparse
 // blocks of 64 or more keys) that is one start token and the mask comes from a
-// few scalar operations; only the chunk a wave copies needs its page looked up.
-// Dead chunks copy the tile's first live chunk and rows at or past the live
-// length re-read their chunk's first row, so LDS never holds non-finite data.
+// few scalar operations; only the chunk a wave copies needs its page looked up,
+// and that lookup is done one iteration early.  Dead chunks copy the tile's
+// first live chunk and rows at or past the live length re-read their chunk's
+// first row, so LDS never holds non-finite data.
 //
-// Per tile and wave:
+// Per tile and 32-row block:
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (M = keys, N = query rows,
 //     K = head dim): every lane holds 16 keys of ONE query row per 32 keys, so
 //     the row max needs one exchange between the two half-waves;
 //   * masks are applied only to tiles that need them (an invalid or cut key,
 //     the causal diagonal, the window edge);
 //   * online softmax in base 2: exp2(s * scale * log2 e - m) as one FMA and one
-//     exp; the running output is rescaled only when some row max moved;
+//     exp; the reference m only moves when a row max passes it by more than a
+//     fixed slack, so the running output is rarely rescaled;
 //   * O^T += V^T P^T: the V^T operand comes from ds_read_b64_tr_b16, which
 //     returns a 4-key x 16-dim block of the row-major V tile column-wise; lane
 //     half h then holds keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key step --
@@ -59,14 +61,27 @@ struct AttnLayout {
   static constexpr int KT = kKvTile;             // keys per tile
   static constexpr int ROWB = D * 2;             // bytes per K / V row
   static constexpr int TILE_B = KT * ROWB;       // bytes of a K (or V) tile
-  static constexpr int NSTAGE = (D == 128 && NW == 8) ? 3 : 2;
-  static constexpr int STAGE_B = 2 * TILE_B;
-  static constexpr int LDS = NSTAGE * STAGE_B;
+  // Tiles of copy lookahead: tile t is copied LA iterations before it is read,
+  // into ring slots (LA+1 per ring) whose previous tile every wave has finished.
+  static constexpr int LA = (D == 128 && NW == 8) ? 2 : 1;
+  static constexpr int NSK = LA + 1;
+  static constexpr int NSV = LA + 1;
+  static constexpr int V_BASE = NSK * TILE_B;
+  static constexpr int LDS = (NSK + NSV) * TILE_B;
   static constexpr int INSTR = TILE_B / 1024;    // 1 KB DMA instructions per K (or V) tile
   static constexpr int KPI = 1024 / ROWB;        // key rows per DMA instruction
   static constexpr int LPK = 64 / KPI;           // lanes per key row in one instruction
   static constexpr int IPW = INSTR / NW;         // K (and V) instructions per wave per tile
 };
+
+// Waves per SIMD that the LDS footprint allows (160 KB per CU).  Telling the
+// compiler keeps it from trimming registers for an occupancy it cannot reach.
+template <int D, int NW>
+constexpr int attn_waves_per_simd() {
+  constexpr int wgs = (160 * 1024) / AttnLayout<D, NW>::LDS;
+  constexpr int w = wgs * NW / 4;
+  return w < 1 ? 1 : (w > 8 ? 8 : w);
+}
 
 // Physical 16-byte piece of logical piece lp in V row `key`, and its inverse.
 // The XOR with 2*(key & 3) separates the four rows of one transpose read; the
@@ -98,29 +113,43 @@ __device__ __forceinline__ void wait_vmcnt() {
 // (global_load_lds_dwordx4; the LDS base is taken from M0, which needs one wait
 // state after the SALU write).  Written as inline assembly so the compiler does
 // not treat every later LDS read as depending on every copy in flight: the
-// kernel orders copies and reads itself with s_waitcnt vmcnt and barriers.
+// kernel orders copies and reads itself with s_waitcnt vmcnt and barriers (both
+// ordered with volatile asm), and the data read here is never written.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+               :: "v"(src), "s"(lds_addr) : "m0");
 }
 
-// One KV tile, wave-uniform.
+// Lanes whose bit is set in the 64-bit scalar mask keep x, the others take y.
+__device__ __forceinline__ float select_lanes(uint64_t mask, float x, float y) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(y), "v"(x), "s"(mask));
+  return r;
+}
+
+// Slack of the softmax reference max, in log2 units.
+constexpr float kRescaleSlack = 8.0f;
+
+// One KV tile, wave-uniform.  CPW = chunks this wave copies (8 / waves).
+template <int CPW>
 struct TileMeta {
   uint64_t M;       // bit k: key k may be admitted (live, valid, inside [k_lo, k_hi))
   int t0;           // first token (contiguous tiles)
-  int t_first;      // first token of the first chunk with an admissible key
   int tmin, tmax;   // token range of the tile's chunks with admissible keys
   int ts[8];        // first token of each chunk (tiles of small sparse blocks)
+  int64_t src[CPW]; // pool offset of the chunk each of this wave's copies reads
+  int tsrc[CPW];    // and its first token
 };
 
 template <int D, int NW, int MODE, bool F32, bool CONTIG>
-__global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(attn_waves_per_simd<D, NW>(), attn_waves_per_simd<D, NW>())))
+attn_fwd_kernel(const AttnParams p) {
   using Lay = AttnLayout<D, NW>;
   constexpr int TILE_M = 32 * NW;
   constexpr int NKS = D / 16;           // S^T k-steps over the head dim
   constexpr int NDB = D / 32;           // 32-row blocks of O^T
   constexpr int IPW = Lay::IPW;
-  constexpr int PD = Lay::NSTAGE - 1;   // tiles in flight ahead of the one computed
   static_assert(Lay::INSTR % NW == 0, "tile instructions must split evenly over waves");
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -233,8 +262,10 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
     return (int64_t)ld_const(ids, pi) * p.kv_page_stride + head_off + (int64_t)slot * D;
   };
 
-  auto tile_meta = [&](int j) -> TileMeta {
-    TileMeta tm;
+  constexpr int CPW = 8 / NW;
+  using TM = TileMeta<CPW>;
+  auto tile_meta = [&](int j) -> TM {
+    TM tm;
     if (CONTIG) {
       int t0;
       if (MODE == kModeBsa) {
@@ -246,20 +277,34 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
       const int lo = min(max(k_lo - t0, 0), 64);
       const int hi = min(max(k_hi - t0, 0), 64);
       uint64_t M = (hi >= 64 ? ~0ull : ((1ull << hi) - 1ull)) & ~(lo >= 64 ? ~0ull : ((1ull << lo) - 1ull));
+      const uint64_t M_range = M;
       if (MODE == kModeBsa && p.valid_bits && M) {
-        // t0 is a multiple of 64 here; the second word exists when t0 + 32 < L
+        // t0 is a multiple of 64 here: keys t0..t0+63 are two whole words; the
+        // second is used only when t0 + 32 < L (its index is clamped to the array)
         const int64_t w = (int64_t)b * p.valid_words + (t0 >> 5);
-        uint64_t bits = ld_const(p.valid_bits, w);
-        if (t0 + 32 < L) bits |= (uint64_t)ld_const(p.valid_bits, w + 1) << 32;
-        M &= bits;
+        const int64_t w_last = (int64_t)p.B * p.valid_words - 1;
+        const uint32_t lo = ld_const(p.valid_bits, w);
+        const uint32_t hi = ld_const(p.valid_bits, w + 1 < w_last ? w + 1 : w_last);
+        M &= (uint64_t)lo | ((t0 + 32 < L) ? (uint64_t)hi << 32 : 0ull);
       }
       tm.M = M;
       tm.t0 = t0;
       const int c_first = M ? (__builtin_ctzll(M) >> 3) : 0;
       const int c_last = M ? ((63 - __builtin_clzll(M)) >> 3) : 0;
-      tm.t_first = t0 + 8 * c_first;
       tm.tmin = t0 + 8 * c_first;
       tm.tmax = t0 + 8 * c_last + 7;
+      if (M) {
+        // chunks outside [k_lo, k_hi) copy the first chunk inside it
+        const int t_r = max(t0, k_lo & ~7);
+#pragma unroll
+        for (int lc = 0; lc < CPW; ++lc) {
+          const int c = wave * CPW + lc;
+          const bool in_range = (M_range >> (8 * c)) & 0xFFu;
+          const int t = in_range ? t0 + 8 * c : t_r;
+          tm.tsrc[lc] = t;
+          tm.src[lc] = token_src(t);
+        }
+      }
     } else {
       uint64_t M = 0;
       int t_first = -1, tmin = 0x7fffffff, tmax = -1;
@@ -282,44 +327,51 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
       }
       tm.M = M;
       tm.t0 = 0;
-      tm.t_first = t_first;
       tm.tmin = tmin;
       tm.tmax = tmax;
+      if (M) {
+        // chunks without an admissible key copy the first chunk with one
+#pragma unroll
+        for (int lc = 0; lc < CPW; ++lc) {
+          const int c = wave * CPW + lc;
+          const int t = ((M >> (8 * c)) & 0xFFu) ? small_chunk_token(j * 8 + c) : t_first;
+          tm.tsrc[lc] = t;
+          tm.src[lc] = token_src(t);
+        }
+      }
     }
     return tm;
   };
 
-  // This wave's share of tile j's copies into stage st.  Lane l of K (V)
+  // This wave's share of tile j's copies into its K and V ring slots.  Lane l of K (V)
   // instruction i writes LDS bytes i*1024 + 16l: row i*KPI + l/LPK, physical
   // piece l%LPK, so it fetches the logical piece stored there.
-  auto issue_tile = [&](const TileMeta& tm, int j, int st) {
-    const uint32_t kst = lds_base + st * Lay::STAGE_B;
-    const uint32_t vst = kst + Lay::TILE_B;
+  auto issue_tile = [&](const TM& tm, int j) {
+    const uint32_t kst = lds_base + (j % Lay::NSK) * Lay::TILE_B;
+    const uint32_t vst = lds_base + Lay::V_BASE + (j % Lay::NSV) * Lay::TILE_B;
 #pragma unroll
     for (int ii = 0; ii < IPW; ++ii) {
       const int i = wave * IPW + ii;
-      const int c = (i * Lay::KPI) >> 3;
-      int t;
-      if ((tm.M >> (8 * c)) & 0xFFu) t = CONTIG ? tm.t0 + 8 * c : small_chunk_token(j * 8 + c);
-      else t = tm.t_first;
-      const int64_t src = token_src(t);
+      const int lc = (ii * Lay::KPI) >> 3;   // = chunk (i * KPI) / 8 - wave * CPW
+      const int t = tm.tsrc[lc];
       const int key = i * Lay::KPI + lane / Lay::LPK;
       const int r = key & 7;
       const int rr = (t + r < L) ? r : 0;
       const int pp = lane % Lay::LPK;
-      lds_dma16(p.k + src + rr * D + (pp ^ (key & 15)) * 8, kst + i * 1024);
-      lds_dma16(p.v + src + rr * D + v_unswz(key, pp) * 8, vst + i * 1024);
+      lds_dma16(p.k + tm.src[lc] + rr * D + (pp ^ (key & 15)) * 8, kst + i * 1024);
+      lds_dma16(p.v + tm.src[lc] + rr * D + v_unswz(key, pp) * 8, vst + i * 1024);
     }
   };
 
   // ---------------- prologue: first tiles in flight, then Q ----------------
-  TileMeta tmr[PD + 1];   // tmr[k] = tile j + k
+  constexpr int LA = Lay::LA;
+  TM tmr[LA + 1];   // tmr[k] = tile j + k
 #pragma unroll
-  for (int k = 0; k < PD; ++k) {
+  for (int k = 0; k <= LA; ++k) {
     tmr[k].M = 0;
     if (k < n_tiles) {
       tmr[k] = tile_meta(k);
-      if (tmr[k].M) issue_tile(tmr[k], k, k);
+      if (tmr[k].M && k < LA) issue_tile(tmr[k], k);
     }
   }
 
@@ -362,153 +414,190 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
   for (int d = 0; d < NDB; ++d)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
-  float m_run = -INFINITY;   // running max of scale*log2(e)*s
+  float m_run = -INFINITY;   // softmax reference, scale*log2(e) units (row max <= m_run + slack)
   float l_run = 0.f;
   const float sl2 = p.scale_log2;
   const int wl = p.window_left;
   const int myp4 = my_p - 4 * hh;        // causal: lane admits tile token tk + 4hh iff tk <= myp4
   const int myw4 = my_p - wl - 4 * hh;   // window: ... iff tk >= myw4
+  const float neg_inf = -INFINITY;
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int st = j % Lay::NSTAGE;
-    // this wave's copies of tile j have landed (later tiles may still fly)
-    if (PD == 2 && j + 1 < n_tiles && tmr[1].M) wait_vmcnt<2 * IPW>();
-    else wait_vmcnt<0>();
-    __syncthreads();     // all of tile j is in LDS; every wave is done with tile j-1
-    tmr[PD].M = 0;
-    if (j + PD < n_tiles) {
-      tmr[PD] = tile_meta(j + PD);
-      if (tmr[PD].M) issue_tile(tmr[PD], j + PD, (j + PD) % Lay::NSTAGE);   // tile j-1's stage
-    }
-    const TileMeta& tm = tmr[0];
-
-    if (wave_rows && tm.M) {
-      const unsigned char* sK = smem + st * Lay::STAGE_B;
-      const unsigned char* sV = sK + Lay::TILE_B;
-      // ---- S^T = K Q^T for two 32-key blocks ----
-      f32x16 sacc[2];
+  // ---------------- phases of one tile ----------------
+  // K fragment of key block kb, k-step s from the K ring slot
+  auto k_frag = [&](int slot, int kb, int s) -> bf16x8 {
+    const unsigned char* sK = smem + slot * Lay::TILE_B;
+    return *(const bf16x8*)(sK + koff[s & 7] + (s >> 3) * 256 + kb * 32 * Lay::ROWB);
+  };
+  // V^T fragment of dim block d, 16-key step s from the V ring slot
+  auto v_frag = [&](int slot, int d, int s) -> bf16x8 {
+    const unsigned char* a = smem + Lay::V_BASE + slot * Lay::TILE_B + voff[d & 3] + (d >> 2) * 256 +
+                             16 * s * Lay::ROWB;
+    const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+    const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(a + 8 * Lay::ROWB));
+    const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
+    u32x4 w;
+    w[0] = y0[0]; w[1] = y0[1]; w[2] = y1[0]; w[3] = y1[1];
+    return as_bf16x8(w);
+  };
+  // S^T for the tile whose K sits in ring slot `slot`
+  // (K fragments are read kKPre k-steps ahead of their MFMAs.)
+  auto compute_s = [&](int slot, f32x16 (&acc)[2]) {
+    constexpr int kKPre = 4;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
+    bf16x8 kr[kKPre][2];
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          const bf16x8 a = *(const bf16x8*)(sK + koff[s & 7] + (s >> 3) * 256 + kb * 32 * Lay::ROWB);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-        }
-      }
-      // ---- masks (element i of block kb is key 32kb + 8(i>>2) + 4hh + (i&3)) ----
-      auto chunk_t = [&](int c) { return CONTIG ? tm.t0 + 8 * c : tm.ts[c]; };
-      if (tm.M != ~0ull) {
-        const uint64_t Mh = hh ? (tm.M >> 4) : tm.M;
+    for (int s = 0; s < kKPre; ++s)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) kr[s][kb] = k_frag(slot, kb, s);
+    // the order written here is kept: the scheduler would otherwise sink
+    // each read to just before its MFMA and expose the LDS latency
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int pos = 32 * kb + 8 * (i >> 2) + (i & 3);
-            if (!((Mh >> pos) & 1)) sacc[kb][i] = -INFINITY;
-          }
-      }
-      if (p.causal && tm.tmax > wp_lo) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (chunk_t(4 * kb + (i >> 2)) + (i & 3) > myp4) sacc[kb][i] = -INFINITY;
-      }
-      if (wl >= 0 && tm.tmin < wp_hi - wl) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (chunk_t(4 * kb + (i >> 2)) + (i & 3) < myw4) sacc[kb][i] = -INFINITY;
-      }
-      // ---- online softmax ----
-      float mx = -INFINITY;
+    for (int s = 0; s < NKS; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s % kKPre][kb], qf[s], acc[kb], 0, 0, 0);
+      if (s + kKPre < NKS) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      float psum = 0.f;
+        for (int kb = 0; kb < 2; ++kb) kr[s % kKPre][kb] = k_frag(slot, kb, s + kKPre);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // masks (element i of block kb is key 32kb + 8(i>>2) + 4hh + (i&3) of the tile)
+  auto mask_s = [&](const TM& tm, f32x16 (&acc)[2]) {
+    auto chunk_t = [&](int c) { return CONTIG ? tm.t0 + 8 * c : tm.ts[c]; };
+    if (tm.M != ~0ull) {
+      // lanes 0-31 take key bit pos, lanes 32-63 bit pos + 4: a scalar lane mask
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(__builtin_fmaf(sacc[kb][i], sl2, -m_use));
-          sacc[kb][i] = e;
-          psum += e;
+          const int pos = 32 * kb + 8 * (i >> 2) + (i & 3);
+          const uint64_t lo = ((tm.M >> pos) & 1) ? 0xFFFFFFFFull : 0ull;
+          const uint64_t hi = ((tm.M >> (pos + 4)) & 1) ? 0xFFFFFFFF00000000ull : 0ull;
+          acc[kb][i] = select_lanes(lo | hi, acc[kb][i], neg_inf);
         }
-      if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {   // some row max moved
-        const float alpha = fast_exp2(m_run - m_use);
-        l_run *= alpha;
+    }
+    if (p.causal && tm.tmax > wp_lo) {
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+        for (int i = 0; i < 16; ++i)
+          if (chunk_t(4 * kb + (i >> 2)) + (i & 3) > myp4) acc[kb][i] = -INFINITY;
+    }
+    if (wl >= 0 && tm.tmin < wp_hi - wl) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (chunk_t(4 * kb + (i >> 2)) + (i & 3) < myw4) acc[kb][i] = -INFINITY;
+    }
+  };
+  // Online softmax of one masked S^T tile: new reference, probabilities packed
+  // as bf16 (P^T operands; lo = P - bf16(P) for fp32 output), and their sum.
+  // The reference only moves when the row max passes it by more than
+  // kRescaleSlack (log2 units), so P <= 2^kRescaleSlack and the rescale of O is
+  // rare; O / l does not depend on the reference.
+  float m_ref, m_use, psum;
+  bf16x8 pb[4], pl[4];
+  auto softmax = [&](f32x16 (&acc)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[kb][i]);
+    mx = half_max(mx);
+    const float m_new = mx * sl2;
+    m_ref = (m_new > m_run + kRescaleSlack) ? m_new : m_run;
+    m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    psum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 w, wl4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float e0 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t], sl2, -m_use));
+        const float e1 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t + 1], sl2, -m_use));
+        psum += e0 + e1;
+        w[t] = cvt_pk_bf16(e0, e1);
+        if (F32)
+          wl4[t] = cvt_pk_bf16(e0 - __uint_as_float(w[t] << 16), e1 - __uint_as_float(w[t] & 0xFFFF0000u));
       }
-      l_run += psum;
-      m_run = m_new;
-
-      // ---- O^T += V^T P^T ----
-      bf16x8 pb[4];
+      pb[s] = as_bf16x8(w);
+      if (F32) pl[s] = as_bf16x8(wl4);
+    }
+  };
+  // move every row's softmax reference to m_ref
+  auto rescale = [&]() {
+    if (__builtin_amdgcn_ballot_w64(m_ref != m_run)) {
+      const float alpha = fast_exp2(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_ref;
+  };
+  // (V fragments of dim block d+1 are read while block d's MFMAs run.)
+  auto compute_pv = [&](int slot) {
+    bf16x8 va[2][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) va[0][s] = v_frag(slot, 0, s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      if (d + 1 < NDB) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) va[(d + 1) & 1][s] = v_frag(slot, d + 1, s);
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        u32x4 w;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          w[t] = cvt_pk_bf16(sacc[s >> 1][8 * (s & 1) + 2 * t], sacc[s >> 1][8 * (s & 1) + 2 * t + 1]);
-        pb[s] = as_bf16x8(w);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d & 1][s], pb[s], oacc[d], 0, 0, 0);
+        if (F32)
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d & 1][s], pl[s], oacc[d], 0, 0, 0);
       }
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        bf16x8 va[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const unsigned char* a = sV + voff[d & 3] + (d >> 2) * 256 + 16 * s * Lay::ROWB;
-          const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(a));
-          const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(a + 8 * Lay::ROWB));
-          const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
-          u32x4 w;
-          w[0] = y0[0]; w[1] = y0[1]; w[2] = y1[0]; w[3] = y1[1];
-          va[s] = as_bf16x8(w);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], pb[s], oacc[d], 0, 0, 0);
-        if (F32) {
-          // fp32 output: add P - bf16(P) as a second bf16 operand (~16-bit P)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const u32x4 hi = __builtin_bit_cast(u32x4, pb[s]);
-            u32x4 w;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const float p0 = sacc[s >> 1][8 * (s & 1) + 2 * t];
-              const float p1 = sacc[s >> 1][8 * (s & 1) + 2 * t + 1];
-              w[t] = cvt_pk_bf16(p0 - __uint_as_float(hi[t] << 16),
-                                 p1 - __uint_as_float(hi[t] & 0xFFFF0000u));
-            }
-            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], as_bf16x8(w), oacc[d], 0, 0, 0);
-          }
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---------------- tile loop ----------------
+  // Iteration j: S_j, masks, softmax and O += V_j P_j.
+  for (int j = 0; j < n_tiles; ++j) {
+    // tile j landed in every wave's share; tiles j+1 .. j+LA-1 may still fly
+    if (LA == 2 && j + 1 < n_tiles && tmr[1].M) wait_vmcnt<2 * IPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();     // ... and is visible; every wave is done with tile j-1
+    if (tmr[LA].M) issue_tile(tmr[LA], j + LA);   // slots of tile j-1
+    if (wave_rows && tmr[0].M) {
+      f32x16 sc[2];
+      compute_s(j % Lay::NSK, sc);
+      mask_s(tmr[0], sc);
+      softmax(sc);
+      rescale();
+      compute_pv(j % Lay::NSV);
     }
 #pragma unroll
-    for (int k = 0; k < PD; ++k) tmr[k] = tmr[k + 1];
+    for (int k = 0; k < LA; ++k) tmr[k] = tmr[k + 1];
+    // metadata of the tile copied next iteration: its scalar loads overlap the
+    // MFMAs still in flight
+    tmr[LA].M = 0;
+    if (j + 1 + LA < n_tiles) tmr[LA] = tile_meta(j + 1 + LA);
   }
 
   // ---------------- epilogue ----------------
+  if (!wave_rows) return;
+  const float l_tot = half_sum(l_run);
+  if (!row_ok) return;
   if (partial_out) {
     // Split-KV decode: this split's unnormalised partial (O, m, l); a separate
     // merge kernel combines the splits.
-    if (!wave_rows) return;
-    const float l_tot = half_sum(l_run);
-    if (!row_ok) return;
     float* dst = p.part + (((int64_t)b * p.Hq + my_hq) * p.num_splits + split) * (D + 4);
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
@@ -524,9 +613,6 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
     }
     return;
   }
-  if (!wave_rows) return;
-  const float l_tot = half_sum(l_run);
-  if (!row_ok) return;
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_tot;
   const int64_t orow = ((int64_t)(tok_base + my_i) * p.Hq + my_hq);
@@ -549,8 +635,8 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const AttnParams p) {
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * d + 8 * g4 + 4 * hh;
         u32x2 w;
-        w[0] = pack_bf16x2(oacc[d][4 * g4] * inv, oacc[d][4 * g4 + 1] * inv);
-        w[1] = pack_bf16x2(oacc[d][4 * g4 + 2] * inv, oacc[d][4 * g4 + 3] * inv);
+        w[0] = cvt_pk_bf16(oacc[d][4 * g4] * inv, oacc[d][4 * g4 + 1] * inv);
+        w[1] = cvt_pk_bf16(oacc[d][4 * g4 + 2] * inv, oacc[d][4 * g4 + 3] * inv);
         *(u32x2*)(o + d0) = w;
       }
   }
