@@ -44,6 +44,44 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# ---------------------------------------------------------------------------- HBM traffic
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def _sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernels):
+    """HBM bytes per launch of the named kernels, from the counter runs recorded
+    in profiles/hbm_traffic.md (FETCH_SIZE and WRITE_SIZE per dispatch, each
+    scaled by what the same counter reads for a plain copy of known size).
+    None when a kernel has no record or its source changed since the record."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    recs = {}
+    for ln in lines:
+        if not ln.startswith("traffic-record:"):
+            continue
+        f = dict(kv.split("=", 1) for kv in ln.split()[1:])
+        recs[f["kernel"]] = f
+    total = 0
+    for k in kernels:
+        r = recs.get(k)
+        if r is None or _sha256([os.path.join(ROOT, x) for x in r["source"].split(",")]) != r["sha256"]:
+            return None
+        total += int(r["bytes_per_launch"])
+    return total
+
+
 def dev_i32(a):
     return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).cuda()
 
@@ -150,7 +188,8 @@ def bench_decode(steps, warmup, W, P):
            "sum_seq_len": int(case.seq_lens.sum()), "num_splits": S, "split_len": split_len,
            "kv_bytes_per_step": kv_bytes}
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(["decode_kernel<128>", "decode_merge_kernel<128>"]),
             "kernel": "decode_kernel<128> + decode_merge_kernel<128> (one step)",
             "per_unit": "4096 B of K+V per live token (Hkv=8, D=128, bf16)"}
     return case, gbs, ms_step, cfg, roof
@@ -185,7 +224,7 @@ def bench_bsa_long(steps, warmup, W, P):
             "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None,
+                         "traffic": measured_traffic(["attn_fwd_kernel<128,8,bsa>"]),
                          "kernel": "attn_fwd_kernel<128,%d,bsa>" % wr.plan.waves}}
 
 
@@ -215,7 +254,8 @@ def bench_prefill(steps, warmup, W, P, D=128, window_left=-1):
             "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None,
+                         "traffic": measured_traffic(
+                             ["attn_fwd_kernel<%d,%d,prefill>" % (D, wr.plan.waves)]),
                          "kernel": "attn_fwd_kernel<%d,%d,prefill>" % (D, wr.plan.waves)}}
 
 
@@ -291,7 +331,20 @@ def bench_sage(steps, warmup, W, P):
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4),
                          "frac_of_bf16_peak": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel": "sage_kernel"}}
+                         "traffic": measured_traffic(["sage_kernel"]), "kernel": "sage_kernel"}}
+
+
+def bench_copy():
+    """A plain 1 GiB device-to-device copy, three times: the calibration run
+    for the FETCH_SIZE / WRITE_SIZE counters (what they read for known bytes)."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"workload": "device copy", "bytes_per_copy": n, "copies": 3}
 
 
 def cpu_baseline_decode(case, budget_s=15.0):
@@ -326,8 +379,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["decode", "bsa", "prefill", "tiny", "sage"], default=None,
-                    help="run one workload only (for profiling)")
+    ap.add_argument("--only", choices=["decode", "bsa", "prefill", "prefill256", "tiny", "sage",
+                                       "copy"], default=None,
+                    help="run one workload only (for profiling; copy = counter calibration)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU component "
@@ -343,8 +397,10 @@ def main(argv=None):
     if a.only and a.only != "decode":
         fn = {"bsa": lambda: bench_bsa_long(a.steps, a.warmup, W, P),
               "prefill": lambda: bench_prefill(a.steps, a.warmup, W, P),
+              "prefill256": lambda: bench_prefill(a.steps, a.warmup, W, P, D=256),
               "tiny": lambda: bench_bsa_tiny(a.steps, a.warmup, W, P),
-              "sage": lambda: bench_sage(a.steps, a.warmup, W, P)}[a.only]
+              "sage": lambda: bench_sage(a.steps, a.warmup, W, P),
+              "copy": bench_copy}[a.only]
         print(json.dumps(fn()), flush=True)
         return 0
 
