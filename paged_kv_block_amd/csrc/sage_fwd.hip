@@ -12,60 +12,137 @@
 //
 // One workgroup = (b, h, query block of 64 rows): two waves of 32 rows.  Per
 // selected KV block (64 tokens, one tile):
-//   * K [64 keys x 128] int8 goes to LDS row-major; S^T = K Q^T runs on
-//     v_mfma_i32_32x32x32_i8 (M = keys, N = query rows, K = 32 dims), so each
-//     lane holds 16 keys of one query row per 32-key half;
+//   * K [64 keys x 128] int8 and V^T [128 dims x 64 keys] fp8 are copied HBM ->
+//     LDS by direct-to-LDS loads (global_load_lds_dwordx4) into a ring of
+//     kNStage blocks, kNStage - 1 blocks ahead of use;
+//   * S^T = K Q^T runs on v_mfma_i32_32x32x32_i8 (M = keys, N = query rows,
+//     K = 32 dims).  The K rows are stored permuted (sage_key_of_row) so that
+//     lane half h's accumulator holds keys 32h .. 32h+31 in order;
 //   * the int32 scores are scaled once per (wave, block): q_scale is constant
 //     over a wave's 32 rows and k_scale over the block;
-//   * online softmax in base 2; P (in [0, 1]) is scaled by 448 and packed to
-//     OCP E4M3 (v_cvt_pk_fp8_f32) as a hi part plus the rounding residual;
-//   * V arrives in HDS layout (tokens contiguous per head dim), which is already
-//     the K-contiguous A operand of O^T += V^T P^T on v_mfma_f32_32x32x64_f8f6f4.
-//     Its 64-byte rows are staged in LDS with the 4-key groups reordered
-//     (even groups, then odd) so that lane half h reads, as 32 contiguous bytes,
-//     exactly the keys {4h + 8a + c} its S^T accumulator holds;
-//   * the epilogue applies v_scale[d] / (448 * l) and writes bf16.
-// The next block's K and V are loaded into registers while the current block
-// computes.
+//   * online softmax in base 2 with the exact running max (P <= 1, so P * 448
+//     keeps E4M3's range for the small weights); P is packed to OCP E4M3
+//     (v_cvt_pk_fp8_f32) as a hi part plus the rounding residual -- E4M3 alone
+//     keeps 3 mantissa bits, too coarse for rows with only a few admitted keys;
+//   * V arrives in HDS layout (tokens contiguous per head dim), which is the
+//     K-contiguous A operand of O^T += V^T P^T on v_mfma_f32_32x32x64_f8f6f4:
+//     lane half h reads the 32 contiguous bytes of keys 32h .. 32h+31, the
+//     same keys (in the same order) its P^T operand holds.  Keys at or past a
+//     partial block's size are zeroed in LDS (their storage may hold NaN codes);
+//   * the epilogue applies v_scale[d] / (448 l) and writes bf16.
+// Workgroups are dealt round-robin over the 8 XCDs; each XCD gets a contiguous
+// run of (head, query block) items so the K/V of the heads it works on stay in
+// its L2.
 #include "device_common.h"
 #include "pkb_internal.h"
 
 namespace pkb {
 
 namespace {
-constexpr int kKRow = 128 + 16;  // LDS bytes per K row (pad: distinct banks for 8 rows)
-constexpr int kVRow = 64 + 16;   // LDS bytes per V^T row (64 fp8 keys + pad)
-constexpr int kLds = 64 * kKRow + 128 * kVRow;
-constexpr float kP8 = 448.f;     // P is stored as P * 448 (the E4M3 maximum)
+constexpr int kKRowB = 128;                // LDS bytes per K row
+constexpr int kVRowB = 64;                 // LDS bytes per V^T row (64 fp8 keys)
+constexpr int kKTile = 64 * kKRowB;        // 8 KB
+constexpr int kVTile = 128 * kVRowB;       // 8 KB
+constexpr int kStage = kKTile + kVTile;
+constexpr int kNStage = 2;
+static_assert(kNStage >= 2 && kNStage <= 4, "wait counts cover up to two blocks in flight");
+constexpr int kLA = kNStage - 1;           // blocks copied ahead of the one computed
+constexpr int kLds = kNStage * kStage;     // 32 KB: four workgroups (two waves per SIMD) per CU
+constexpr float kP8 = 448.f;               // P * 448 is stored (E4M3 max 448)
+constexpr int kXcds = 8;
 }  // namespace
 
 __device__ __forceinline__ int sage_block_size(const SageParams& p, int b, int h, int beta) {
   if (p.bs_rank == 0) return 64;
-  if (p.bs_rank == 1) return p.block_sizes[beta];
-  if (p.bs_rank == 2) return p.block_sizes[(int64_t)b * p.nkb + beta];
-  return p.block_sizes[((int64_t)b * p.H + h) * p.nkb + beta];
+  if (p.bs_rank == 1) return ld_const(p.block_sizes, beta);
+  if (p.bs_rank == 2) return ld_const(p.block_sizes, (int64_t)b * p.nkb + beta);
+  return ld_const(p.block_sizes, ((int64_t)b * p.H + h) * p.nkb + beta);
 }
 
-__global__ void __launch_bounds__(128) sage_kernel(const SageParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
-  unsigned char* sK = smem;
-  unsigned char* sV = smem + 64 * kKRow;
+// Key held by LDS K row rho: the S^T accumulator of lane half h holds rows
+// 32kb + 8a + 4h + c (element 4a + c of block kb), which is made key
+// 32h + 16kb + 4a + c.
+__device__ __forceinline__ int sage_key_of_row(int rho) {
+  const int kb = rho >> 5, a = (rho >> 3) & 3, h = (rho >> 2) & 1, c = rho & 3;
+  return 32 * h + 16 * kb + 4 * a + c;
+}
+
+__device__ __forceinline__ void sage_dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr) : "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void sage_wait_vmcnt() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+sage_kernel(const SageParams p) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
   const int hh = lane >> 5;
   const int ql = lane & 31;
-  const int r = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int64_t bh = (int64_t)b * p.H + h;
 
-  const int64_t row_base = (int64_t)r * p.capacity;
-  const int32_t* idx = p.index + (bh * p.nqb) * p.capacity + row_base;
-  const int n = p.nums ? p.nums[bh * p.nqb + r] : p.block_sparse_num;
+  // XCD-aware item order: workgroup g runs on XCD g % 8 and is that XCD's
+  // (g / 8)-th; XCD x takes items [x * per, (x + 1) * per), head-major.
+  const int total = p.nqb * p.H * p.B;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int item = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (item >= total) return;
+  const int r = item % p.nqb;
+  const int64_t bh = item / p.nqb;
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+
+  const int32_t* idx = p.index + (bh * p.nqb + r) * p.capacity;
+  const int n = p.nums ? ld_const(p.nums, bh * p.nqb + r) : p.block_sparse_num;
 
   const int row = r * 64 + wave * 32 + ql;
   const bool row_ok = row < p.Sq;
 
+  // block metadata: id and valid-token count (0: nothing to do)
+  struct BlockMeta { int beta, kv; };
+  auto block_meta = [&](int t) -> BlockMeta {
+    BlockMeta m;
+    m.beta = ld_const(idx, t);
+    m.kv = min(sage_block_size(p, b, h, m.beta), p.Sk - m.beta * 64);
+    return m;
+  };
+  // this wave's share of block t's copies into ring stage t % kNStage: K rows
+  // (permuted, pieces swizzled by (row >> 1) & 7) and V^T rows (pieces swizzled
+  // by (row >> 2) & 3); K rows past Sk re-read the block's first row
+  auto issue_block = [&](const BlockMeta& m, int t) {
+    const uint32_t kst = lds_base + (t % kNStage) * kStage;
+    const uint32_t vst = kst + kKTile;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = wave * 4 + ii;
+      const int rho = 8 * i + (lane >> 3);
+      const int kp = (lane & 7) ^ ((rho >> 1) & 7);
+      int key = sage_key_of_row(rho);
+      if (m.beta * 64 + key >= p.Sk) key = 0;
+      sage_dma16(p.k + ((bh * p.Sk + m.beta * 64 + key) * 128 + kp * 16), kst + i * 1024);
+      const int d = 16 * i + (lane >> 2);
+      const int vp = (lane & 3) ^ ((d >> 2) & 3);
+      sage_dma16(p.v + ((bh * 128 + d) * p.Skp + m.beta * 64 + vp * 16), vst + i * 1024);
+    }
+  };
+
+  // ---- prologue: first blocks in flight, then Q ----
+  BlockMeta bm[kLA + 1];
+#pragma unroll
+  for (int k = 0; k <= kLA; ++k) {
+    bm[k].kv = 0;
+    if (k < n) {
+      bm[k] = block_meta(k);
+      if (bm[k].kv > 0 && k < kLA) issue_block(bm[k], k);
+    }
+  }
   // Q^T fragments (B operand of S^T): k-step s covers dims 32s..32s+31; lane
   // half hh holds dims 32s + 16hh .. +15.
   i32x4 qf[4];
@@ -79,6 +156,7 @@ __global__ void __launch_bounds__(128) sage_kernel(const SageParams p) {
     }
   }
   const float qs = p.q_scale[bh * p.qs_len + (r * 64 + wave * 32) / 32];
+  sage_wait_vmcnt<0>();   // no load issued before the loop is pending inside it
 
   f32x16 oacc[4];
 #pragma unroll
@@ -86,148 +164,136 @@ __global__ void __launch_bounds__(128) sage_kernel(const SageParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-
-  // staging: thread t loads K row t/2 half t%2 (64 B) and V^T row t (64 B)
-  const int krow = tid >> 1, khalf = tid & 1;
-  u32x4 kreg[4], vreg[4];
-  auto load_block = [&](int beta, int kv) {
-    const int8_t* kp = p.k + (bh * p.Sk + (int64_t)beta * 64 + krow) * 128 + 64 * khalf;
-    const bool kok = krow < kv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (kok) x = ld_global_16(kp + 16 * i);
-      kreg[i] = x;
-    }
-    const uint8_t* vp = p.v + (bh * 128 + tid) * p.Skp + (int64_t)beta * 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vreg[i] = ld_global_16(vp + 16 * i);
-  };
-  auto store_block = [&](int kv) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(sK + krow * kKRow + 64 * khalf + 16 * i) = kreg[i];
-    // zero the bytes of keys >= kv (their storage may hold anything), then put
-    // even 4-key groups first and odd ones second
-    uint32_t w[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[4 * i + e] = vreg[i][e];
-#pragma unroll
-    for (int gq = 0; gq < 16; ++gq) {
-      const int keep = min(max(kv - 4 * gq, 0), 4);          // valid keys in this group
-      const uint32_t mask = keep >= 4 ? 0xFFFFFFFFu : ((1u << (8 * keep)) - 1u);
-      w[gq] &= mask;
-    }
-    u32x4 e0 = {w[0], w[2], w[4], w[6]}, e1 = {w[8], w[10], w[12], w[14]};
-    u32x4 o0 = {w[1], w[3], w[5], w[7]}, o1 = {w[9], w[11], w[13], w[15]};
-    unsigned char* vr = sV + tid * kVRow;
-    *(u32x4*)(vr + 0) = e0;
-    *(u32x4*)(vr + 16) = e1;
-    *(u32x4*)(vr + 32) = o0;
-    *(u32x4*)(vr + 48) = o1;
-  };
-
   const float sl2 = p.scale_log2;
-  int beta = n > 0 ? idx[0] : 0;
-  int kv = 0;
-  if (n > 0) {
-    kv = min(sage_block_size(p, b, h, beta), p.Sk - beta * 64);
-    load_block(beta, kv);
-  }
+  const int koff_row = ql * kKRowB;
+  const int kswz = (ql >> 1) & 7;                    // rows 32kb + ql: same low bits
+  const int vswz = (ql >> 2) & 3;                    // rows 32d + ql
+
   for (int t = 0; t < n; ++t) {
-    const int cur_kv = kv;
-    const int cur_beta = beta;
-    __syncthreads();                 // previous block's LDS reads are done
-    store_block(cur_kv);
-    __syncthreads();
-    if (t + 1 < n) {                 // next block in flight during this one
-      beta = idx[t + 1];
-      kv = min(sage_block_size(p, b, h, beta), p.Sk - beta * 64);
-      load_block(beta, kv);
+    // block t landed in every wave's share; blocks t+1 .. t+kLA-1 may still fly
+    int ahead = 0;
+#pragma unroll
+    for (int k = 1; k < kLA; ++k) ahead += (t + k < n && bm[k].kv > 0) ? 1 : 0;
+    if (ahead == 0) sage_wait_vmcnt<0>();
+    else if (ahead == 1) sage_wait_vmcnt<8>();
+    else sage_wait_vmcnt<16>();
+    __syncthreads();                 // ... and is visible; block t-1's stage is free
+    if (bm[kLA].kv > 0) issue_block(bm[kLA], t + kLA);
+    const int kv = bm[0].kv;
+    const unsigned char* sK = smem + (t % kNStage) * kStage;
+    const unsigned char* sV = sK + kKTile;
+    if (kv > 0 && kv < 64) {
+      // partial block: zero the V bytes of keys >= kv (row d = tid)
+      unsigned char* vr = (unsigned char*)sV + tid * kVRowB;
+#pragma unroll
+      for (int lp = 0; lp < 4; ++lp) {
+        if (16 * lp + 15 < kv) continue;
+        const int pp = lp ^ ((tid >> 2) & 3);
+        u32x4 x = *(u32x4*)(vr + pp * 16);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int k0 = 16 * lp + 4 * w;
+          const int keep = min(max(kv - k0, 0), 4);
+          x[w] &= keep >= 4 ? 0xFFFFFFFFu : ((1u << (8 * keep)) - 1u);
+        }
+        *(u32x4*)(vr + pp * 16) = x;
+      }
+      __syncthreads();
     }
-    const float ks = p.k_scale[bh * p.nkb + cur_beta];
-    const float sc = qs * ks * sl2;
-
-    // ---- S^T = K Q^T, two 32-key halves ----
-    i32x16 sacc[2];
+    if (kv > 0) {
+      const float ks = ld_const(p.k_scale, bh * p.nkb + bm[0].beta);
+      const float sc = qs * ks * sl2;
+      // ---- S^T = K Q^T, two 32-key blocks ----
+      i32x4 kf[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0;
-      const unsigned char* kr = sK + (32 * kb + ql) * kKRow + 16 * hh;
+        for (int s = 0; s < 4; ++s)
+          kf[kb][s] = *(const i32x4*)(sK + kb * 32 * kKRowB + koff_row + (((2 * s + hh) ^ kswz) * 16));
+      __builtin_amdgcn_sched_barrier(0);
+      i32x16 sacc[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const i32x4 a = *(const i32x4*)(kr + 32 * s);
-        sacc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], sacc[kb], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sacc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][s], qf[s], sacc[kb], 0, 0, 0);
+      // V^T fragments, read while the S MFMAs run
+      i32x8 vf[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const unsigned char* vr = sV + (32 * d + ql) * kVRowB;
+        const u32x4 a0 = *(const u32x4*)(vr + (((2 * hh) ^ vswz) * 16));
+        const u32x4 a1 = *(const u32x4*)(vr + (((2 * hh + 1) ^ vswz) * 16));
+        vf[d][0] = a0[0]; vf[d][1] = a0[1]; vf[d][2] = a0[2]; vf[d][3] = a0[3];
+        vf[d][4] = a1[0]; vf[d][5] = a1[1]; vf[d][6] = a1[2]; vf[d][7] = a1[3];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- scale, mask keys >= kv (element (kb, i) is key 32hh + 16kb + i) ----
+      float sv[2][16];
+      float mx = -INFINITY;
+      const int kvh = kv - 32 * hh;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = (16 * kb + i < kvh) ? (float)sacc[kb][i] * sc : -INFINITY;
+          sv[kb][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = half_max(mx);
+      const float m_ref = fmaxf(m_run, mx);
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = fast_exp2(sv[kb][i] - m_use);
+          sv[kb][i] = e;
+          psum += e;
+        }
+      if (__builtin_amdgcn_ballot_w64(m_ref != m_run)) {
+        const float alpha = fast_exp2(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      }
+      l_run += psum;
+      m_run = m_ref;
+      // ---- P^T -> fp8 (x 448) as hi + lo parts, slot j = 16kb + i ----
+      i32x8 pb, pl;
+#pragma unroll
+      for (int wd = 0; wd < 8; ++wd) {
+        const int kb = wd >> 2;
+        const int i0 = 4 * (wd & 3);
+        const float x0 = sv[kb][i0] * kP8, x1 = sv[kb][i0 + 1] * kP8;
+        const float x2 = sv[kb][i0 + 2] * kP8, x3 = sv[kb][i0 + 3] * kP8;
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
+        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23[0], x3 - h23[1], lo, true);
+        pb[wd] = hi;
+        pl[wd] = lo;
+      }
+      // ---- O^T += V^T P^T: four 32-dim blocks, K = 64 keys ----
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        oacc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[d], pb, oacc[d], 0, 0, 0, 0, 0, 0);
+        oacc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[d], pl, oacc[d], 0, 0, 0, 0, 0, 0);
       }
     }
-    // ---- scale, mask keys >= kv, online softmax ----
-    float sv[2][16];
-    float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const float x = key < cur_kv ? (float)sacc[kb][i] * sc : -INFINITY;
-        sv[kb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = half_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(sv[kb][i] - m_use);
-        sv[kb][i] = e;
-        psum += e;
-      }
-    if (m_new != m_run) {
-      const float alpha = fast_exp2(m_run - m_use);
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-    }
-    l_run += psum;
-    m_run = m_new;
-
-    // ---- P^T -> fp8 (x448), as hi + lo parts: E4M3 alone keeps 3 mantissa
-    // bits, too coarse for rows with only a few admitted keys; hi + lo gives
-    // about 7.  Slot j < 16: first 32-key half, else second. ----
-    i32x8 pb, pl;
-#pragma unroll
-    for (int wd = 0; wd < 8; ++wd) {
-      const int kb = wd >> 2;
-      const int i0 = 4 * (wd & 3);
-      const float x0 = sv[kb][i0] * kP8, x1 = sv[kb][i0 + 1] * kP8;
-      const float x2 = sv[kb][i0 + 2] * kP8, x3 = sv[kb][i0 + 3] * kP8;
-      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
-      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], 0, false);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23[0], x3 - h23[1], lo, true);
-      pb[wd] = hi;
-      pl[wd] = lo;
-    }
-    // ---- O^T += V^T P^T: four 32-dim blocks, K = 64 keys ----
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const unsigned char* vrp = sV + (32 * d + ql) * kVRow + 32 * hh;
-      const u32x4 a0 = *(const u32x4*)(vrp);
-      const u32x4 a1 = *(const u32x4*)(vrp + 16);
-      i32x8 a;
-      a[0] = a0[0]; a[1] = a0[1]; a[2] = a0[2]; a[3] = a0[3];
-      a[4] = a1[0]; a[5] = a1[1]; a[6] = a1[2]; a[7] = a1[3];
-      oacc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[d], 0, 0, 0, 0, 0, 0);
-      oacc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pl, oacc[d], 0, 0, 0, 0, 0, 0);
-    }
+    for (int k = 0; k < kLA; ++k) bm[k] = bm[k + 1];
+    bm[kLA].kv = 0;
+    if (t + 1 + kLA < n) bm[kLA] = block_meta(t + 1 + kLA);
   }
 
   // ---- epilogue: O = O^T * v_scale[d] / (448 l) -> bf16 [B, H, Sq, 128] ----
@@ -250,10 +316,13 @@ __global__ void __launch_bounds__(128) sage_kernel(const SageParams p) {
 }
 
 hipError_t launch_sage(const SageParams& p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.nqb * p.H * p.B;
+  const int64_t per = (total + kXcds - 1) / kXcds;
+  if (per * kXcds > 0x7fffffff) return hipErrorInvalidValue;
   SageParams arg = p;
   void* args[] = {(void*)&arg};
-  return hipLaunchKernel((const void*)sage_kernel, dim3(p.nqb, p.H, p.B), dim3(128), args, 0,
-                         stream);
+  return hipLaunchKernel((const void*)sage_kernel, dim3((unsigned)(per * kXcds)), dim3(128), args,
+                         kLds, stream);
 }
 
 }  // namespace pkb
