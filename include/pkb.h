@@ -144,7 +144,8 @@ typedef struct {
   int32_t waves;            /* wavefronts per workgroup (32 packed rows each) */
   int32_t tile_m;           /* packed query rows per workgroup = 32 * waves */
   int32_t tiles_per_brow;   /* ceil(rows_per_brow / tile_m) */
-  int32_t grid_x, grid_y, grid_z;
+  int32_t grid_x, grid_y, grid_z; /* work units: (query tile, KV head, request); the
+                                      launch deals them over the XCDs as a 1-D grid */
   int32_t kernel_id;
 } bsa_plan_t;
 

@@ -85,7 +85,8 @@ int bsa_run(const bsa_plan_t* plan, const void* q, const void* k, const void* v,
   p.out_f32 = a.out_dtype == PKB_FP32;
   p.scale_log2 = scale_or_default(sm_scale, a.D) * 1.4426950408889634f;
   p.out_scale = 1.0f;
-  dim3 grid(plan->grid_x, plan->grid_y, plan->grid_z);
+  const int64_t total = (int64_t)plan->grid_x * plan->grid_y * plan->grid_z;
+  dim3 grid((unsigned)(((total + 7) / 8) * 8), 1, 1);
   return hip_status(pkb::launch_attn(p, a.D, plan->waves, pkb::kModeBsa, grid,
                                      (hipStream_t)stream));
 }

@@ -160,15 +160,24 @@ attn_fwd_kernel(const AttnParams p) {
   const int wave = wave_uniform(tid >> 6);
   const int hh = lane >> 5;        // half-wave
   const int ql = lane & 31;        // query row inside the wave
-  const int kvh = blockIdx.y;
+  int kvh = blockIdx.y;
   const int G = p.G;
 
   // ---------------- work item ----------------
   int b, qlen, tok_base, m_begin, m_end, split = 0;
   int bip_lo = 0, n_sel = 0;
   if (MODE == kModeBsa) {
-    b = blockIdx.z;
-    const int x = p.nqb * p.tiles_per_brow - 1 - (int)blockIdx.x;   // late rows first
+    // XCD-aware order: the 1-D grid deals workgroups round-robin over the 8
+    // XCDs; XCD c takes items [c * per, (c + 1) * per) of the (b, kvh, x) list
+    const int nx = p.nqb * p.tiles_per_brow;
+    const int total = nx * p.Hkv * p.B;
+    const int per = (total + 7) >> 3;
+    const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (item >= total) return;
+    const int xi = item % nx;
+    kvh = (item / nx) % p.Hkv;
+    b = item / (nx * p.Hkv);
+    const int x = nx - 1 - xi;   // late rows first
     const int r = x / p.tiles_per_brow;
     const int t = x - r * p.tiles_per_brow;
     qlen = p.Sq;
