@@ -292,6 +292,44 @@ def make_decode(seed, B, Hq, Hkv, D, seq_lens, page_size, mask="dense", window_l
                       bmm1_scale, bmm2_scale, name)
 
 
+@dataclass
+class DecodeQCase:
+    """Multi-token (fixed SQ or packed) decode inputs with CSR page IDs."""
+    q: torch.Tensor                 # [B, SQ, Hq, D] (fixed) or [total_q, Hq, D] (packed)
+    k: torch.Tensor                 # [P, Hkv, ps, D]
+    v: torch.Tensor
+    kv_indptr: np.ndarray           # [B+1] int32
+    kv_indices: np.ndarray          # int32
+    seq_lens: np.ndarray            # [B] int32
+    qo_indptr: np.ndarray | None    # [B+1] int32 (packed) or None (fixed SQ)
+    seq_len_q: int                  # SQ (fixed) or max_seq_len_q (packed)
+    max_seq_len: int
+    mask: str
+    window_left: int
+    name: str = ""
+
+
+def make_decode_q(seed, B, Hq, Hkv, D, seq_lens, page_size, seq_len_q=None, qlens=None,
+                  mask="causal", window_left=-1, extra_pages=0, name=""):
+    """Fixed SQ (qlens None) or packed per-request query lengths `qlens`."""
+    rng = _rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    if qlens is None:
+        q = randn_bf16(rng, (B, seq_len_q, Hq, D))
+        qo = None
+        sq = int(seq_len_q)
+    else:
+        qlens = np.asarray(qlens, dtype=np.int32)
+        qo = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+        q = randn_bf16(rng, (int(qo[-1]), Hq, D))
+        sq = int(seq_len_q or qlens.max())
+    indptr, indices, P = csr_page_table(rng, seq_lens, page_size, extra_pages)
+    k = randn_bf16(rng, (P, Hkv, page_size, D))
+    v = randn_bf16(rng, (P, Hkv, page_size, D))
+    return DecodeQCase(q, k, v, indptr, indices, seq_lens, qo, sq, int(seq_lens.max()), mask,
+                       window_left, name)
+
+
 # ----------------------------------------------------------------------------
 # The five named workloads
 # ----------------------------------------------------------------------------

@@ -264,6 +264,49 @@ def decode_reference(q, k, v, kv_indptr, kv_indices, seq_lens, mask="dense",
     return out, lse
 
 
+def decode_q_reference(q, k, v, kv_indptr, kv_indices, seq_lens, qo_indptr=None,
+                       mask="causal", window_left=-1, bmm1_scale=None, bmm2_scale=1.0):
+    """Multi-token decode over CSR pages ("prims_ts_batch_decode_with_kv_cache",
+    description: seq_len_q > 1 uses token-major [B, SQ, Hq, D]; with qo_indptr,
+    packed [total_q, Hq, D] where request b owns rows qo_indptr[b]:qo_indptr[b+1]).
+    Query i of request b sits at position L - qlen + i.  Returns (out, lse) in the
+    query's layout ([..., Hq, D] and [..., Hq])."""
+    q = _f64(q); k = _f64(k); v = _f64(v)
+    kv_indptr = _i64(kv_indptr); kv_indices = _i64(kv_indices); seq_lens = _i64(seq_lens)
+    B = len(seq_lens)
+    Hkv = k.shape[1]
+    D = q.shape[-1]
+    Hq = q.shape[-2]
+    G = Hq // Hkv
+    scale = _default_scale(bmm1_scale, D)
+    causal = (mask == "causal")
+    if qo_indptr is None:
+        SQ = q.shape[1]
+        qo = np.arange(B + 1, dtype=np.int64) * SQ
+        qp = q.reshape(B * SQ, Hq, D)
+    else:
+        qo = _i64(qo_indptr)
+        qp = q
+    out = np.zeros(qp.shape)
+    lse = np.full(qp.shape[:2], -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        qlen = int(qo[b + 1] - qo[b])
+        Kb = gather_csr(k, kv_indptr, kv_indices, b, L)
+        Vb = gather_csr(v, kv_indptr, kv_indices, b, L)
+        p = L - qlen + np.arange(qlen)
+        adm = position_mask(p, np.arange(L), causal, window_left)
+        for g in range(Hkv):
+            qr = qp[qo[b]:qo[b + 1], g * G:(g + 1) * G, :].reshape(-1, D)
+            o, s = attend(qr, Kb[:, g, :], Vb[:, g, :], np.repeat(adm, G, axis=0), scale,
+                          bmm2_scale)
+            out[qo[b]:qo[b + 1], g * G:(g + 1) * G] = o.reshape(qlen, G, D)
+            lse[qo[b]:qo[b + 1], g * G:(g + 1) * G] = s.reshape(qlen, G)
+    if qo_indptr is None:
+        return out.reshape(q.shape), lse.reshape(B, q.shape[1], Hq)
+    return out, lse
+
+
 # ----------------------------------------------------------------------------
 # Sage-style prequantized block-sparse attention
 # ----------------------------------------------------------------------------

@@ -146,3 +146,39 @@ def decode_bruteforce(q, k, v, kv_indptr, kv_indices, seq_lens, mask="dense",
                 vals.append(v[page][g][j % ps])
             out[b][h], lse[b][h] = _row_softmax(q[b][h], keys, vals, scale, bmm2_scale)
     return out, lse
+
+
+def decode_q_bruteforce(q, k, v, kv_indptr, kv_indices, seq_lens, qo_indptr,
+                        mask="causal", window_left=-1, bmm1_scale=None, bmm2_scale=1.0):
+    """Packed multi-token decode, q [total_q, Hq, D], one loop per admitted key."""
+    q, k, v = _lst(q), _lst(k), _lst(v)
+    kv_indptr, kv_indices = _lst(kv_indptr), _lst(kv_indices)
+    seq_lens, qo = _lst(seq_lens), _lst(qo_indptr)
+    T, Hq, D = len(q), len(q[0]), len(q[0][0])
+    Hkv, ps = len(k[0]), len(k[0][0])
+    grp = Hq // Hkv
+    scale = bmm1_scale if bmm1_scale else 1.0 / math.sqrt(D)
+    out = [None] * T
+    lse = [None] * T
+    for b in range(len(seq_lens)):
+        L = seq_lens[b]
+        qlen = qo[b + 1] - qo[b]
+        for i in range(qlen):
+            row = qo[b] + i
+            pos = L - qlen + i
+            out[row] = [None] * Hq
+            lse[row] = [None] * Hq
+            for h in range(Hq):
+                g = h // grp
+                keys, vals = [], []
+                for j in range(L):
+                    if mask == "causal" and j > pos:
+                        continue
+                    if window_left >= 0 and j < pos - window_left:
+                        continue
+                    page = kv_indices[kv_indptr[b] + j // ps]
+                    keys.append(k[page][g][j % ps])
+                    vals.append(v[page][g][j % ps])
+                out[row][h], lse[row][h] = _row_softmax(q[row][h], keys, vals, scale,
+                                                        bmm2_scale)
+    return out, lse

@@ -322,40 +322,73 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
 
 // Merge of the chunk partials, one workgroup per (request, query head): LSE-
 // weighted sum over chunks c < ceil(seq_len / CH), in chunk order.
+// Merge of one (request, query head): LSE-weighted sum of its live splits'
+// partials.  Lane s holds split s's (m, l) (64 splits per pass), so the max and
+// the weights take one load round trip; the O accumulation then issues the
+// partial rows of eight splits at a time, each lane owning D/64 dims.
 template <int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(const MergeParams p) {
+  constexpr int PER = D / 64;
+  constexpr int ROW = D + 4;
   const int bh = blockIdx.x;
+  const int lane = threadIdx.x;
   const int b = bh / p.Hq;
   const int L = p.seq_lens[b];
   const int n = min(p.num_splits, (L + p.split_len - 1) / p.split_len);
-  const float* base = p.part + (int64_t)bh * p.num_splits * (D + 4);
+  const float* base = p.part + (int64_t)bh * p.num_splits * ROW;
   float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, base[s * (D + 4) + D]);
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int s = s0 + lane;
+    float m = s < n ? base[(int64_t)s * ROW + D] : -INFINITY;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    M = fmaxf(M, m);
+  }
   float lsum = 0.f;
-  constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
   for (int t = 0; t < PER; ++t) acc[t] = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < n; ++s) {
-      const float w = fast_exp2(base[s * (D + 4) + D] - M);
-      lsum += base[s * (D + 4) + D + 1] * w;
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const int s = s0 + lane;
+      float w = 0.f, wl = 0.f;
+      if (s < n) {
+        w = fast_exp2(base[(int64_t)s * ROW + D] - M);
+        wl = w * base[(int64_t)s * ROW + D + 1];
+      }
 #pragma unroll
-      for (int t = 0; t < PER; ++t) acc[t] += w * base[s * (D + 4) + threadIdx.x * PER + t];
+      for (int o = 32; o >= 1; o >>= 1) wl += __shfl_xor(wl, o);
+      lsum += wl;
+      const int cnt = min(64, n - s0);
+      for (int k0 = 0; k0 < cnt; k0 += 8) {
+        float x[8][PER];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int t = 0; t < PER; ++t)
+            x[k][t] = (k0 + k < cnt) ? base[(int64_t)(s0 + k0 + k) * ROW + lane * PER + t] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          // k0 + k <= 63: k0 < cnt <= 64 steps by 8
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k0 + k));
+#pragma unroll
+          for (int t = 0; t < PER; ++t) acc[t] += wk * x[k][t];
+        }
+      }
     }
   }
   const bool empty = !(lsum > 0.f);
   const float inv = empty ? 0.f : p.out_scale / lsum;
   if (p.out_f32) {
-    float* o = (float*)p.out + (int64_t)bh * D + threadIdx.x * PER;
+    float* o = (float*)p.out + (int64_t)bh * D + lane * PER;
 #pragma unroll
     for (int t = 0; t < PER; ++t) o[t] = acc[t] * inv;
   } else {
-    uint16_t* o = (uint16_t*)p.out + (int64_t)bh * D + threadIdx.x * PER;
+    uint16_t* o = (uint16_t*)p.out + (int64_t)bh * D + lane * PER;
 #pragma unroll
     for (int t = 0; t < PER; t += 2) *(uint32_t*)(o + t) = pack_bf16x2(acc[t] * inv, acc[t + 1] * inv);
   }
-  if (p.lse && threadIdx.x == 0) p.lse[bh] = empty ? -INFINITY : (M + __log2f(lsum)) * kLn2;
+  if (p.lse && lane == 0) p.lse[bh] = empty ? -INFINITY : (M + __log2f(lsum)) * kLn2;
 }
 
 template <int D>

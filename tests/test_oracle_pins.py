@@ -440,3 +440,67 @@ def test_sage_zero_count_rows_and_partial_blocks():
     ob, _ = BF._row_softmax(list(Qd[b, h, i]), [list(Kd[b, h, t]) for t in toks],
                             [list(Vd[b, h, t]) for t in toks], 1 / math.sqrt(128), 1.0)
     cmp(out[b, h, i], ob, 1e-12)
+
+
+# ---------------------------------------------------------------- multi-token decode
+
+def _csr_to_table(case):
+    ps = case.k.shape[2]
+    npg = [-(-int(L) // ps) for L in case.seq_lens]
+    tab = np.full((len(npg), max(npg)), -1, dtype=np.int64)
+    for b, n in enumerate(npg):
+        tab[b, :n] = case.kv_indices[case.kv_indptr[b]:case.kv_indptr[b] + n]
+    return tab
+
+
+@pytest.mark.parametrize("mask,w", [("causal", -1), ("causal", 2), ("dense", -1)])
+def test_decode_q_oracle_matches_bruteforce(mask, w):
+    case = W.make_decode_q(21, 3, 4, 2, 8, [5, 12, 9], 4, qlens=[2, 4, 1], mask=mask,
+                           window_left=w)
+    args = (f64(case.q), f64(case.k), f64(case.v), case.kv_indptr, case.kv_indices,
+            case.seq_lens, case.qo_indptr)
+    o, l = A.decode_q_reference(*args, mask=mask, window_left=w, bmm1_scale=0.4,
+                                bmm2_scale=1.5)
+    ob, lb = BF.decode_q_bruteforce(*args, mask=mask, window_left=w, bmm1_scale=0.4,
+                                    bmm2_scale=1.5)
+    cmp(o, ob)
+    cmp(l, lb)
+
+
+@pytest.mark.parametrize("mask,w", [("dense", -1), ("causal", 7)])
+def test_decode_q_single_token_is_decode(mask, w):
+    """SQ = 1 reduces to single-token decode at position L - 1."""
+    case = W.make_decode_q(22, 3, 8, 2, 16, [1, 17, 40], 8, seq_len_q=1, mask=mask,
+                           window_left=w)
+    args = (f64(case.q), f64(case.k), f64(case.v), case.kv_indptr, case.kv_indices,
+            case.seq_lens)
+    o, l = A.decode_q_reference(*args, mask=mask, window_left=w)
+    od, ld = A.decode_reference(f64(case.q)[:, 0], *args[1:], mask=mask, window_left=w)
+    cmp(o[:, 0], od)
+    cmp(l[:, 0], ld)
+
+
+def test_decode_q_matches_prefill_on_the_same_pages():
+    """Packed multi-token decode over CSR pages = packed prefill over the same
+    pages written as a block table (both bottom-right aligned)."""
+    case = W.make_decode_q(23, 4, 6, 3, 16, [9, 33, 20, 5], 8, qlens=[3, 8, 1, 5],
+                           mask="causal", window_left=4)
+    o, l = A.decode_q_reference(f64(case.q), f64(case.k), f64(case.v), case.kv_indptr,
+                                case.kv_indices, case.seq_lens, case.qo_indptr,
+                                mask="causal", window_left=4)
+    op, lp = A.prefill_reference(f64(case.q), f64(case.k), f64(case.v), case.qo_indptr,
+                                 _csr_to_table(case), case.seq_lens, mask="causal",
+                                 window_left=4)
+    cmp(o, op)
+    cmp(l, lp)
+
+
+def test_decode_q_fixed_layout_is_packed_layout():
+    """[B, SQ, Hq, D] is the packed layout with qo_indptr = b * SQ."""
+    case = W.make_decode_q(24, 3, 4, 1, 8, [6, 10, 4], 4, seq_len_q=4, mask="causal")
+    args = (f64(case.k), f64(case.v), case.kv_indptr, case.kv_indices, case.seq_lens)
+    o, l = A.decode_q_reference(f64(case.q), *args)
+    qo = np.arange(4) * 4
+    op, lp = A.decode_q_reference(f64(case.q).reshape(12, 4, 8), *args, qo_indptr=qo)
+    cmp(o.reshape(12, 4, 8), op)
+    cmp(l.reshape(12, 4), lp)
