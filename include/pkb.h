@@ -12,6 +12,7 @@
  *   - single-token paged decode with caller scratch
  *     (page "flashinfer.attention.prims_ts.prims_ts_batch_decode_with_kv_cache")
  *                                                        -> paged_decode_validate / _workspace_size / _run
+ *     multi-token (fixed SQ or packed qo_indptr) decode   -> paged_decode_q_validate / _workspace_size / _run
  *   - prequantized Sage-style block-sparse attention
  *     (page "flashinfer.cute_dsl.sparse.bsa_attn_sm120.bsa_attn_sm120_blk64_sage_fwd")
  *                                                        -> bsa_sage_validate / bsa_sage_run
@@ -286,6 +287,51 @@ int paged_decode_run(const void* query, const void* k, const void* v,
                      float bmm2_scale, int32_t out_dtype, void* out, float* lse,
                      void* workspace, size_t workspace_bytes, int32_t num_cus,
                      void* stream);
+
+/* Multi-token decode (decode page, description: for seq_len_q > 1 query and
+ * output are token-major [B, SQ, Hq, D]; with qo_indptr they are packed
+ * [total_q, Hq, D] and request b owns rows qo_indptr[b]:qo_indptr[b+1];
+ * max_seq_len_q is the static bound).  Query i of request b sits at position
+ * seq_len - qlen + i (bottom-right); causal needs qlen <= seq_len.
+ *
+ * Split policy and workspace: same chunk policy as paged_decode_workspace_size;
+ * fp32 partials [B, max_q, Hq, num_splits, D+4] (max_q = seq_len_q, or
+ * max_seq_len_q when packed), written before they are read (no initialisation
+ * needed). */
+int paged_decode_q_workspace_size(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t max_seq_len, int32_t page_size, int32_t num_cus,
+                                  size_t* bytes, int32_t* num_splits, int32_t* split_len);
+
+/* Host validation (host copies).  Order: kv_indptr (CSR), seq_lens in
+ * [1, max_seq_len], then if qo_indptr_h is given: qo_indptr[0] == 0 (index 0),
+ * every delta in [1, max_seq_len_q] (index b+1), qo_indptr[B] == total_q
+ * (index B); then, for causal, every query length <= seq_len (SEQ_LENS, b);
+ * then each request's CSR sufficiency and live IDs as paged_decode_validate.
+ * Static errors (PKB_ERR_ARG): seq_len_q < 1 without qo_indptr, or
+ * max_seq_len_q < 1 / total_q < 1 with it. */
+int paged_decode_q_validate(int32_t B, int32_t num_pages, int32_t page_size,
+                            int32_t max_seq_len, const int32_t* paged_kv_indptr_h,
+                            const int32_t* paged_kv_indices_h, int64_t n_indices,
+                            const int32_t* seq_lens_h, const int32_t* qo_indptr_h,
+                            int64_t total_q, int32_t seq_len_q, int32_t max_seq_len_q,
+                            int32_t mask_type, pkb_bad_t* bad);
+
+/* Trusted run.  query [B, seq_len_q, Hq, D] bf16 when qo_indptr is NULL, else
+ * [total_q, Hq, D] with qo_indptr a device [B+1] int32 array satisfying the
+ * packed-offset contract above (it is read on the device only); out in the
+ * query's layout (out_dtype); lse [tokens, Hq] fp32 or NULL; other arguments as
+ * paged_decode_run; workspace of at least paged_decode_q_workspace_size()
+ * bytes for max_q = seq_len_q (fixed) or max_seq_len_q (packed). */
+int paged_decode_q_run(const void* query, const void* k, const void* v,
+                       int64_t kv_page_stride, int64_t kv_head_stride,
+                       const int32_t* paged_kv_indptr, const int32_t* paged_kv_indices,
+                       const int32_t* seq_lens, const int32_t* qo_indptr, int32_t B,
+                       int32_t seq_len_q, int32_t max_seq_len_q, int32_t Hq, int32_t Hkv,
+                       int32_t D, int32_t num_pages, int32_t page_size, int32_t max_seq_len,
+                       int32_t mask_type, int32_t window_left, float bmm1_scale,
+                       float bmm2_scale, int32_t out_dtype, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, int32_t num_cus,
+                       void* stream);
 
 /* ======================================================================== */
 /* Sage-style prequantized block-sparse attention                            */

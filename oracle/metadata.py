@@ -307,6 +307,54 @@ def decode_validate(B, P, ps, max_seq_len, kv_indptr, kv_indices, seq_lens):
     return OK
 
 
+def decode_q_policy(B, max_q, Hq, Hkv, D, max_seq_len, page_size, num_cus):
+    """Multi-token decode: the same chunk policy; partials [B, max_q, Hq, S, D+4]."""
+    if max_q < 1:
+        return PKB_ERR_ARG, 0, 0, 0
+    st, nbytes, S, CH = decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus)
+    if st != PKB_OK:
+        return st, 0, 0, 0
+    return PKB_OK, nbytes * max_q, S, CH
+
+
+def decode_q_validate(B, P, ps, max_seq_len, kv_indptr, kv_indices, seq_lens, qo_indptr,
+                      total_q, seq_len_q, max_seq_len_q, causal):
+    """Decode page, description: the packed-offset contract (start at zero,
+    strictly increasing, every delta at most max_seq_len_q, end at the query
+    row count) and, for causal, every query length no greater than seq_len."""
+    if qo_indptr is not None:
+        if max_seq_len_q < 1 or total_q < 1:
+            return PKB_ERR_ARG, F_NONE, -1
+    elif seq_len_q < 1:
+        return PKB_ERR_ARG, F_NONE, -1
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    r = _check_csr(B, P, ps, kv_indptr, kv_indices, seq_lens)
+    if r:
+        return r
+    for b in range(B):
+        if not (1 <= seq_lens[b] <= max_seq_len):
+            return _bad(F_SEQ_LENS, b)
+    if qo_indptr is not None:
+        qo = np.asarray(qo_indptr, dtype=np.int64)
+        if qo[0] != 0:
+            return _bad(F_QO_INDPTR, 0)
+        for b in range(B):
+            d = qo[b + 1] - qo[b]
+            if d < 1 or d > max_seq_len_q:
+                return _bad(F_QO_INDPTR, b + 1)
+        if qo[B] != total_q:
+            return _bad(F_QO_INDPTR, B)
+    if causal:
+        for b in range(B):
+            qlen = (qo_indptr[b + 1] - qo_indptr[b]) if qo_indptr is not None else seq_len_q
+            if qlen > seq_lens[b]:
+                return _bad(F_SEQ_LENS, b)
+    r = _check_pages(B, P, ps, kv_indptr, kv_indices, seq_lens)
+    if r:
+        return r
+    return OK
+
+
 # ----------------------------------------------------------------------------
 # Sage
 # ----------------------------------------------------------------------------

@@ -22,6 +22,9 @@ from .ops import (  # noqa: E402
     bsa_sage_validate,
     bsa_validate,
     num_cus,
+    paged_decode_q_run,
+    paged_decode_q_validate,
+    paged_decode_q_workspace_size,
     paged_decode_run,
     paged_decode_validate,
     paged_decode_workspace_size,
@@ -36,6 +39,7 @@ __all__ = [
     "batch_decode_with_paged_kv_cache", "batch_prefill_with_paged_kv_cache",
     "block_sparse_attention_with_paged_kv_cache", "bsa_attn_blk64_sage_fwd", "bsa_plan",
     "bsa_run", "bsa_sage_run", "bsa_sage_validate", "bsa_validate", "num_cus",
+    "paged_decode_q_run", "paged_decode_q_validate", "paged_decode_q_workspace_size",
     "paged_decode_run", "paged_decode_validate", "paged_decode_workspace_size",
     "paged_prefill_plan", "paged_prefill_run", "paged_prefill_validate", "split_kv_cache",
 ]

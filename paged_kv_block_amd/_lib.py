@@ -87,6 +87,17 @@ _SIGS = {
                                  c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_float, c_float, c_int32,
                                  c_void_p, c_void_p, c_void_p, c_size_t, c_int32, c_void_p]),
+    "paged_decode_q_workspace_size": (c_int, [c_int32, c_int32, c_int32, c_int32, c_int32,
+                                              c_int32, c_int32, c_int32, POINTER(c_size_t),
+                                              POINTER(c_int32), POINTER(c_int32)]),
+    "paged_decode_q_validate": (c_int, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                        c_int64, c_void_p, c_void_p, c_int64, c_int32, c_int32,
+                                        c_int32, POINTER(Bad)]),
+    "paged_decode_q_run": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                   c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                   c_int32, c_float, c_float, c_int32, c_void_p, c_void_p,
+                                   c_void_p, c_size_t, c_int32, c_void_p]),
     "bsa_sage_validate": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p,
                                   c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(Bad)]),
     "bsa_sage_run": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -29,6 +29,28 @@ inline float scale_or_default(float s, int D) {
   return (s > 0.f && isfinite(s)) ? s : 1.0f / sqrtf((float)D);
 }
 
+// Merge of split partials [B, maxq, Hq, S, D+4] into out / lse.
+int launch_merge(float* part, const int32_t* seq_lens, const int32_t* qo_indptr, void* out,
+                 float* lse, int B, int maxq, int Sq, int Hq, int S, int split_len,
+                 int out_dtype, float out_scale, int D, hipStream_t s) {
+  pkb::MergeParams mp;
+  memset(&mp, 0, sizeof(mp));
+  mp.part = part;
+  mp.seq_lens = seq_lens;
+  mp.qo_indptr = qo_indptr;
+  mp.out = out;
+  mp.lse = lse;
+  mp.B = B;
+  mp.Hq = Hq;
+  mp.num_splits = S;
+  mp.split_len = split_len;
+  mp.maxq = maxq;
+  mp.Sq = Sq;
+  mp.out_f32 = out_dtype == PKB_FP32;
+  mp.out_scale = out_scale;
+  return hip_status(pkb::launch_decode_merge(mp, D, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -224,26 +246,81 @@ int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv
     p.window_left = window_left;
     p.num_splits = S;
     p.split_len = split_len;
+    p.Sq = 1;
+    p.maxq = 1;
     p.out_f32 = out_dtype == PKB_FP32;
     p.scale_log2 = sl2;
     p.out_scale = bmm2_scale;
     hipError_t e = pkb::launch_attn(p, D, 4, pkb::kModeDecode, grid, s);
     if (e != hipSuccess) return hip_status(e);
   }
-  if (S > 1) {
-    pkb::MergeParams mp;
-    mp.part = part;
-    mp.seq_lens = seq_lens;
-    mp.out = out;
-    mp.lse = lse;
-    mp.B = B;
-    mp.Hq = Hq;
-    mp.num_splits = S;
-    mp.split_len = split_len;
-    mp.out_f32 = out_dtype == PKB_FP32;
-    mp.out_scale = bmm2_scale;
-    return hip_status(pkb::launch_decode_merge(mp, D, s));
-  }
+  if (S > 1) return launch_merge(part, seq_lens, nullptr, out, lse, B, 1, 1, Hq, S, split_len,
+                                 out_dtype, bmm2_scale, D, s);
+  return PKB_OK;
+}
+
+int paged_decode_q_run(const void* query, const void* k, const void* v, int64_t kv_page_stride,
+                       int64_t kv_head_stride, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, const int32_t* seq_lens,
+                       const int32_t* qo_indptr, int32_t B, int32_t seq_len_q,
+                       int32_t max_seq_len_q, int32_t Hq, int32_t Hkv, int32_t D,
+                       int32_t num_pages, int32_t page_size, int32_t max_seq_len,
+                       int32_t mask_type, int32_t window_left, float bmm1_scale,
+                       float bmm2_scale, int32_t out_dtype, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, int32_t num_cus, void* stream) {
+  const int32_t maxq = qo_indptr ? max_seq_len_q : seq_len_q;
+  size_t need = 0;
+  int32_t S = 0, split_len = 0;
+  int st = paged_decode_q_workspace_size(B, maxq, Hq, Hkv, D, max_seq_len, page_size, num_cus,
+                                         &need, &S, &split_len);
+  if (st) return st;
+  if (num_pages < 1 || B > 65535) return PKB_ERR_ARG;
+  if (mask_type != PKB_MASK_DENSE && mask_type != PKB_MASK_CAUSAL) return PKB_ERR_ARG;
+  if (window_left < -1 || (window_left >= 0 && mask_type != PKB_MASK_CAUSAL)) return PKB_ERR_ARG;
+  if (out_dtype != PKB_BF16 && out_dtype != PKB_FP32) return PKB_ERR_DTYPE;
+  if (!query || !k || !v || !kv_indptr || !kv_indices || !seq_lens || !out) return PKB_ERR_ARG;
+  if (kv_page_stride < (int64_t)Hkv * page_size * D || kv_head_stride < (int64_t)page_size * D)
+    return PKB_ERR_SHAPE;
+  if (!isfinite(bmm2_scale)) return PKB_ERR_ARG;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKB_ERR_WORKSPACE;
+  // row tiles of the general kernel in decode mode (4 waves x 32 packed rows)
+  const int64_t rtiles = cdiv((int64_t)maxq * (Hq / Hkv), 128);
+  if (rtiles * S > 0x7fffffff) return PKB_ERR_UNSUPPORTED;
+  float* part = S > 1 ? (float*)workspace : nullptr;
+  const hipStream_t s = (hipStream_t)stream;
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = (const uint16_t*)query;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.out = out;
+  p.lse = lse;
+  p.part = part;
+  p.kv_indptr = kv_indptr;
+  p.kv_indices = kv_indices;
+  p.qo_indptr = qo_indptr;
+  p.seq_lens = seq_lens;
+  p.kv_page_stride = kv_page_stride;
+  p.kv_head_stride = kv_head_stride;
+  p.B = B;
+  p.Sq = seq_len_q;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.page_size = page_size;
+  p.causal = mask_type == PKB_MASK_CAUSAL;
+  p.window_left = window_left;
+  p.num_splits = S;
+  p.split_len = split_len;
+  p.maxq = maxq;
+  p.out_f32 = out_dtype == PKB_FP32;
+  p.scale_log2 = scale_or_default(bmm1_scale, D) * 1.4426950408889634f;
+  p.out_scale = bmm2_scale;
+  dim3 grid((unsigned)(rtiles * S), Hkv, B);
+  hipError_t e = pkb::launch_attn(p, D, 4, pkb::kModeDecode, grid, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (S > 1) return launch_merge(part, seq_lens, qo_indptr, out, lse, B, maxq, seq_len_q, Hq, S,
+                                 split_len, out_dtype, bmm2_scale, D, s);
   return PKB_OK;
 }
 

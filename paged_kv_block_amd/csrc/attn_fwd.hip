@@ -196,12 +196,19 @@ attn_fwd_kernel(const AttnParams p) {
     qlen = p.qo_indptr[b + 1] - tok_base;
     m_end = min(m_begin + TILE_M, qlen * G);
   } else {
+    // split-KV decode: blockIdx.x = row tile * splits + split, one request per z
     b = blockIdx.z;
-    split = blockIdx.x;
-    qlen = 1;
-    tok_base = b;
-    m_begin = 0;
-    m_end = G;
+    const int rt = (int)blockIdx.x / p.num_splits;
+    split = (int)blockIdx.x - rt * p.num_splits;
+    if (p.qo_indptr) {
+      tok_base = p.qo_indptr[b];
+      qlen = p.qo_indptr[b + 1] - tok_base;
+    } else {
+      qlen = p.Sq;
+      tok_base = b * p.Sq;
+    }
+    m_begin = rt * TILE_M;
+    m_end = min(m_begin + TILE_M, qlen * G);
   }
   const int L = p.seq_lens[b];
   const bool partial_out = (MODE == kModeDecode) && p.num_splits > 1;
@@ -607,7 +614,7 @@ attn_fwd_kernel(const AttnParams p) {
   if (partial_out) {
     // Split-KV decode: this split's unnormalised partial (O, m, l); a separate
     // merge kernel combines the splits.
-    float* dst = p.part + (((int64_t)b * p.Hq + my_hq) * p.num_splits + split) * (D + 4);
+    float* dst = p.part + ((((int64_t)b * p.maxq + my_i) * p.Hq + my_hq) * p.num_splits + split) * (D + 4);
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll

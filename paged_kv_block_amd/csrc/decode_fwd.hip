@@ -322,20 +322,24 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
 
 // Merge of the chunk partials, one workgroup per (request, query head): LSE-
 // weighted sum over chunks c < ceil(seq_len / CH), in chunk order.
-// Merge of one (request, query head): LSE-weighted sum of its live splits'
-// partials.  Lane s holds split s's (m, l) (64 splits per pass), so the max and
+// Merge of one (request, query token, query head): LSE-weighted sum of its live
+// splits' partials.  Lane s holds split s's (m, l) (64 splits per pass), so the max and
 // the weights take one load round trip; the O accumulation then issues the
 // partial rows of eight splits at a time, each lane owning D/64 dims.
 template <int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(const MergeParams p) {
   constexpr int PER = D / 64;
   constexpr int ROW = D + 4;
-  const int bh = blockIdx.x;
   const int lane = threadIdx.x;
-  const int b = bh / p.Hq;
+  const int hq = (int)blockIdx.x % p.Hq;
+  const int i = ((int)blockIdx.x / p.Hq) % p.maxq;
+  const int b = (int)blockIdx.x / (p.Hq * p.maxq);
+  const int qlen = p.qo_indptr ? p.qo_indptr[b + 1] - p.qo_indptr[b] : p.Sq;
+  if (i >= qlen) return;
+  const int64_t bh = ((int64_t)(p.qo_indptr ? p.qo_indptr[b] : b * p.Sq) + i) * p.Hq + hq;
   const int L = p.seq_lens[b];
   const int n = min(p.num_splits, (L + p.split_len - 1) / p.split_len);
-  const float* base = p.part + (int64_t)bh * p.num_splits * ROW;
+  const float* base = p.part + (int64_t)blockIdx.x * p.num_splits * ROW;
   float M = -INFINITY;
   for (int s0 = 0; s0 < n; s0 += 64) {
     const int s = s0 + lane;
@@ -406,7 +410,9 @@ hipError_t launch_decode(const DecodeParams& p, int D, int grid, hipStream_t str
 }
 
 hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream) {
-  dim3 grid(p.B * p.Hq);
+  const int64_t n = (int64_t)p.B * p.maxq * p.Hq;
+  if (n > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)n);
   MergeParams arg = p;
   void* args[] = {(void*)&arg};
   if (D == 128) return hipLaunchKernel((const void*)decode_merge_kernel<128>, grid, dim3(64), args, 0, stream);

@@ -308,6 +308,50 @@ int paged_decode_validate(int32_t B, int32_t num_pages, int32_t page_size, int32
   return check_live_pages(B, num_pages, page_size, kv_indptr, kv_indices, seq_lens, bad);
 }
 
+int paged_decode_q_workspace_size(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t max_seq_len, int32_t page_size, int32_t num_cus,
+                                  size_t* bytes, int32_t* num_splits, int32_t* split_len) {
+  if (max_q < 1) return PKB_ERR_ARG;
+  size_t one = 0;
+  int st = paged_decode_workspace_size(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, &one,
+                                       num_splits, split_len);
+  if (st) return st;
+  // fp32 partials [B, max_q, Hq, S, D+4]
+  if (bytes) *bytes = one * (size_t)max_q;
+  return PKB_OK;
+}
+
+int paged_decode_q_validate(int32_t B, int32_t num_pages, int32_t page_size, int32_t max_seq_len,
+                            const int32_t* kv_indptr, const int32_t* kv_indices, int64_t n_indices,
+                            const int32_t* seq_lens, const int32_t* qo_indptr, int64_t total_q,
+                            int32_t seq_len_q, int32_t max_seq_len_q, int32_t mask_type,
+                            pkb_bad_t* bad) {
+  clear_bad(bad);
+  if (B < 1 || num_pages < 1 || page_size < 1 || !kv_indptr || !seq_lens) return PKB_ERR_ARG;
+  if (max_seq_len < 1 || max_seq_len > PKB_MAX_SEQ_LEN) return PKB_ERR_ARG;
+  if (n_indices > 0 && !kv_indices) return PKB_ERR_ARG;
+  if (mask_type != PKB_MASK_DENSE && mask_type != PKB_MASK_CAUSAL) return PKB_ERR_ARG;
+  if (qo_indptr ? (max_seq_len_q < 1 || total_q < 1) : seq_len_q < 1) return PKB_ERR_ARG;
+  int st = check_indptr(B, kv_indptr, n_indices, PKB_FIELD_KV_INDPTR, bad);
+  if (st) return st;
+  for (int b = 0; b < B; ++b)
+    if (seq_lens[b] < 1 || seq_lens[b] > max_seq_len) return set_bad(bad, PKB_FIELD_SEQ_LENS, b);
+  if (qo_indptr) {
+    if (qo_indptr[0] != 0) return set_bad(bad, PKB_FIELD_QO_INDPTR, 0);
+    for (int b = 0; b < B; ++b) {
+      const int64_t d = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+      if (d < 1 || d > max_seq_len_q) return set_bad(bad, PKB_FIELD_QO_INDPTR, b + 1);
+    }
+    if ((int64_t)qo_indptr[B] != total_q) return set_bad(bad, PKB_FIELD_QO_INDPTR, B);
+  }
+  if (mask_type == PKB_MASK_CAUSAL)
+    for (int b = 0; b < B; ++b) {
+      const int64_t qlen = qo_indptr ? (int64_t)qo_indptr[b + 1] - qo_indptr[b] : seq_len_q;
+      if (qlen > seq_lens[b]) return set_bad(bad, PKB_FIELD_SEQ_LENS, b);
+    }
+  return check_live_pages(B, num_pages, page_size, kv_indptr, kv_indices, seq_lens, bad);
+}
+
 // ------------------------------------------------------------------ sage
 
 int bsa_sage_validate(const int32_t* index, int32_t capacity, int32_t block_sparse_num,

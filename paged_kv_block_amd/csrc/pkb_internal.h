@@ -19,12 +19,12 @@ struct AttnParams {
   const uint16_t* v;
   void* out;                  // [tokens, Hq, D] bf16 or fp32
   float* lse;                 // [tokens, Hq] or null
-  float* part;                // decode split partials [B, Hq, S, D+4] or null
+  float* part;                // decode split partials [B, maxq, Hq, S, D+4] or null
   const int32_t* kv_indptr;   // CSR page IDs (bsa, decode)
   const int32_t* kv_indices;
   const int32_t* block_tables;  // row-strided table (prefill)
   const int32_t* seq_lens;
-  const int32_t* qo_indptr;     // prefill
+  const int32_t* qo_indptr;     // prefill; multi-token decode (null: Sq rows per request)
   const int32_t* block_indptr;  // bsa [B, Hkv, nqb+1]
   const int32_t* block_indices;
   const uint32_t* valid_bits;   // bsa [B, valid_words] or null
@@ -34,6 +34,7 @@ struct AttnParams {
   int qbs, kvbs, nqb, tiles_per_brow, rows_per_brow, valid_words;
   int causal, window_left;
   int num_splits, split_len;
+  int maxq;           // decode: query rows per request in the partials workspace
   int out_f32;
   float scale_log2;   // softmax scale * log2(e)
   float out_scale;
@@ -63,11 +64,13 @@ struct DecodeParams {
 };
 
 struct MergeParams {
-  const float* part;
+  const float* part;            // [B, maxq, Hq, num_splits, D+4]
   const int32_t* seq_lens;
+  const int32_t* qo_indptr;     // packed query rows, or null: Sq rows per request
   void* out;
   float* lse;
   int B, Hq, num_splits, split_len, out_f32;
+  int maxq, Sq;
   float out_scale;
 };
 

@@ -19,6 +19,7 @@ from . import _lib as C
 from ._lib import Bad, BsaPlan, BsaStaticArgs, PrefillPlan, PrefillStaticArgs, check, lib
 
 _DTYPE = {torch.bfloat16: C.PKB_BF16, torch.float32: C.PKB_FP32}
+_MASK = {"dense": C.PKB_MASK_DENSE, "causal": C.PKB_MASK_CAUSAL}
 
 
 def _stream(device=None) -> int:
@@ -364,6 +365,79 @@ def batch_decode_with_paged_kv_cache(query, kv_cache, workspace_buffer, paged_kv
                             max_seq_len, workspace_buffer, mask_type=mask_type,
                             window_left=window_left, bmm1_scale=bmm1_scale,
                             bmm2_scale=bmm2_scale, out=out, lse=lse)
+
+
+# =============================================================================
+# Multi-token decode (fixed seq_len_q or packed qo_indptr)
+# =============================================================================
+
+def paged_decode_q_workspace_size(B, max_q, Hq, Hkv, D, max_seq_len, page_size, num_cus_=None):
+    nb = ctypes.c_size_t(0)
+    S = ctypes.c_int32(0)
+    sl = ctypes.c_int32(0)
+    check(lib().paged_decode_q_workspace_size(B, max_q, Hq, Hkv, D, max_seq_len, page_size,
+                                              num_cus_ if num_cus_ is not None else num_cus(),
+                                              ctypes.byref(nb), ctypes.byref(S),
+                                              ctypes.byref(sl)),
+          "paged_decode_q_workspace_size")
+    return nb.value, S.value, sl.value
+
+
+def paged_decode_q_validate(B, num_pages, page_size, max_seq_len, paged_kv_indptr,
+                            paged_kv_indices, seq_lens, *, qo_indptr=None, total_q=0,
+                            seq_len_q=0, max_seq_len_q=0, mask_type="causal",
+                            raise_on_error=True):
+    ip, ix, sl = _host_i32(paged_kv_indptr), _host_i32(paged_kv_indices), _host_i32(seq_lens)
+    qo = None if qo_indptr is None else _host_i32(qo_indptr)
+    bad = Bad()
+    st = lib().paged_decode_q_validate(B, num_pages, page_size, max_seq_len, _hp(ip), _hp(ix),
+                                       ix.size, _hp(sl), _hp(qo), int(total_q), int(seq_len_q),
+                                       int(max_seq_len_q), _MASK[mask_type], ctypes.byref(bad))
+    if raise_on_error:
+        check(st, "paged_decode_q_validate", bad)
+    return st, bad.field, bad.index
+
+
+def paged_decode_q_run(query, kv_cache, paged_kv_indptr, paged_kv_indices, seq_lens, max_seq_len,
+                       workspace, *, qo_indptr=None, max_seq_len_q=0, mask_type="causal",
+                       window_left=-1, bmm1_scale=None, bmm2_scale=1.0, out=None, lse=None,
+                       num_cus_=None, stream=None):
+    """query [B, Sq, Hq, D] (fixed) or [total_q, Hq, D] with device ``qo_indptr``."""
+    kp, vp, pst, hst, P, Hkv, ps, D, dt, dev = split_kv_cache(kv_cache)
+    _need(query.dtype == torch.bfloat16 and dt == torch.bfloat16 and query.is_contiguous(),
+          "query must be contiguous bf16 matching the cache")
+    if qo_indptr is None:
+        _need(query.dim() == 4 and query.shape[3] == D, "query must be [B, Sq, Hq, D]")
+        B, Sq, Hq = query.shape[0], query.shape[1], query.shape[2]
+        tokens = B * Sq
+    else:
+        _need(query.dim() == 3 and query.shape[2] == D, "query must be [total_q, Hq, D]")
+        _dev_i32(qo_indptr, "qo_indptr")
+        B, Sq, Hq = qo_indptr.numel() - 1, 0, query.shape[1]
+        tokens = query.shape[0]
+        _need(max_seq_len_q >= 1, "max_seq_len_q is required with qo_indptr")
+    for t, n in ((paged_kv_indptr, "paged_kv_indptr"), (paged_kv_indices, "paged_kv_indices"),
+                 (seq_lens, "seq_lens")):
+        _dev_i32(t, n)
+    if out is None:
+        out = torch.empty_like(query)
+    _need(out.is_contiguous() and out.shape == query.shape and out.dtype in _DTYPE,
+          "out must be contiguous bf16 or fp32 in the query's layout")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and lse.numel() == tokens * Hq and lse.is_contiguous(),
+              "lse must be fp32 [tokens, Hq]")
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().paged_decode_q_run(_ptr(query), kp, vp, pst, hst, _ptr(paged_kv_indptr),
+                                  _ptr(paged_kv_indices), _ptr(seq_lens), _ptr(qo_indptr), B,
+                                  int(Sq), int(max_seq_len_q), Hq, Hkv, D, P, ps,
+                                  int(max_seq_len), _MASK[mask_type], int(window_left),
+                                  float(bmm1_scale or 0.0), float(bmm2_scale),
+                                  _DTYPE[out.dtype], _ptr(out), _ptr(lse), ws_ptr, ws_bytes,
+                                  num_cus_ if num_cus_ is not None else num_cus(query.device),
+                                  stream if stream is not None else _stream(query.device))
+    check(st, "paged_decode_q_run")
+    return out
 
 
 # =============================================================================

@@ -119,3 +119,29 @@ def oracle_decode(case, requests=None):
                               case.seq_lens, mask=case.mask, window_left=case.window_left,
                               bmm1_scale=case.bmm1_scale, bmm2_scale=case.bmm2_scale,
                               requests=requests)
+
+
+def run_decode_q(case, out_dtype=torch.bfloat16, num_cus=None):
+    """Multi-token decode of a DecodeQCase through paged_decode_q_run."""
+    q = case.q.to(DEV)
+    Hq, D = q.shape[-2], q.shape[-1]
+    B = len(case.seq_lens)
+    ncu = num_cus if num_cus is not None else P.num_cus()
+    nbytes, S, _ = P.paged_decode_q_workspace_size(B, case.seq_len_q, Hq, case.k.shape[1], D,
+                                                   case.max_seq_len, case.k.shape[2], ncu)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    out = torch.empty(q.shape, dtype=out_dtype, device=DEV)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+    qo = None if case.qo_indptr is None else dev_i32(case.qo_indptr)
+    P.paged_decode_q_run(q, (case.k.to(DEV), case.v.to(DEV)), dev_i32(case.kv_indptr),
+                         dev_i32(case.kv_indices), dev_i32(case.seq_lens), case.max_seq_len, ws,
+                         qo_indptr=qo, max_seq_len_q=case.seq_len_q, mask_type=case.mask,
+                         window_left=case.window_left, out=out, lse=lse, num_cus_=ncu)
+    torch.cuda.synchronize()
+    return out, lse, S
+
+
+def oracle_decode_q(case):
+    return A.decode_q_reference(case.q, case.k, case.v, case.kv_indptr, case.kv_indices,
+                                case.seq_lens, qo_indptr=case.qo_indptr, mask=case.mask,
+                                window_left=case.window_left)

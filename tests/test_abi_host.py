@@ -307,6 +307,64 @@ def test_decode_validate_matches_spec():
     assert n_bad > 80
 
 
+def test_decode_q_policy_matches_spec():
+    rng = np.random.default_rng(4)
+    for _ in range(1000):
+        B = int(rng.integers(1, 300)); Hkv = int(rng.choice([1, 2, 8])); Hq = Hkv * int(rng.choice([1, 4, 16]))
+        D = int(rng.choice([128, 256, 64])); msl = int(rng.choice([1, 64, 65, 8192, M.MAX_SEQ_LEN]))
+        ps = int(rng.choice([8, 16, 12])); cus = int(rng.choice([80, 256]))
+        mq = int(rng.choice([0, 1, 2, 7, 64]))
+        want = M.decode_q_policy(B, mq, Hq, Hkv, D, msl, ps, cus)
+        nb = ctypes.c_size_t(); s = ctypes.c_int32(); l = ctypes.c_int32()
+        st = P.lib().paged_decode_q_workspace_size(B, mq, Hq, Hkv, D, msl, ps, cus, ctypes.byref(nb),
+                                                   ctypes.byref(s), ctypes.byref(l))
+        assert st == want[0]
+        if st == 0:
+            assert (nb.value, s.value, l.value) == want[1:]
+
+
+def test_decode_q_validate_matches_spec():
+    rng = np.random.default_rng(5)
+    case = W.make_decode_q(11, 4, 8, 2, 128, [5, 40, 3, 77], 16, qlens=[2, 6, 3, 1],
+                           extra_pages=3)
+    n_bad = 0
+    for t in range(300):
+        ip, ix, sl = case.kv_indptr.copy(), case.kv_indices.copy(), case.seq_lens.copy()
+        qo = case.qo_indptr.copy()
+        total, sq, msq, causal = int(qo[-1]), 0, 6, bool(rng.random() < 0.7)
+        packed = t % 7 != 6
+        k = t % 8
+        if t < 2:
+            pass
+        elif k == 0:
+            ix[rng.integers(0, ix.size)] = int(rng.choice([-1, case.k.shape[0]]))
+        elif k == 1:
+            ip[rng.integers(0, ip.size)] += int(rng.choice([-1, 1, 2]))
+        elif k == 2:
+            sl[rng.integers(0, sl.size)] = int(rng.choice([0, -3, 78, 200, 2]))
+        elif k == 3:
+            qo[rng.integers(0, qo.size)] += int(rng.choice([-1, 1, 3]))
+        elif k == 4:
+            msq = int(rng.choice([0, 3, 5]))
+        elif k == 5:
+            total = int(rng.choice([0, total - 1, total + 1]))
+        else:
+            sq = int(rng.choice([0, 1, 3, 4, 6]))
+        if not packed:
+            sq = sq or 2
+        want = M.decode_q_validate(4, case.k.shape[0], 16, 100, ip, ix, sl,
+                                   qo if packed else None, total, sq, msq, causal)
+        st, f, i = P.paged_decode_q_validate(4, case.k.shape[0], 16, 100, ip, ix, sl,
+                                             qo_indptr=qo if packed else None, total_q=total,
+                                             seq_len_q=sq, max_seq_len_q=msq,
+                                             mask_type="causal" if causal else "dense",
+                                             raise_on_error=False)
+        got = (st, f, i) if st == M.PKB_ERR_METADATA else (st, 0, -1)
+        assert got == want, (t, packed, causal, got, want)
+        n_bad += want[0] != 0
+    assert n_bad > 100
+
+
 # ----------------------------------------------------------------------------- sage
 
 def test_sage_validate_matches_spec():

@@ -12,7 +12,8 @@ import torch
 
 from gen import workloads as W
 from tests.gpu_util import (TOL_BF16, TOL_F32, TOL_LSE, assert_close, f64, oracle_bsa,
-                            oracle_decode, oracle_prefill, run_bsa, run_decode, run_prefill)
+                            oracle_decode, oracle_decode_q, oracle_prefill, run_bsa, run_decode,
+                            run_decode_q, run_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -215,3 +216,31 @@ def test_batch_decode_sampled():
     assert_close(f64(out[reqs]), ref_o, TOL_BF16, f"out (splits={S})")
     assert_close(f64(lse[reqs]), ref_l, TOL_LSE, "lse")
     assert torch.isfinite(out.float()).all()
+
+
+# ----------------------------------------------------------------------------- multi-token decode
+
+DECODE_Q_SWEEP = [
+    # B, Hq, Hkv, D, seq_lens, ps, SQ (fixed) or qlens (packed), mask, w, num_cus
+    (4, 32, 8, 128, [4, 63, 1000, 3000], 16, 4, "causal", -1, 256),
+    (2, 8, 1, 256, [40, 64], 16, 3, "dense", -1, 256),            # one split
+    (4, 32, 8, 128, [10, 500, 2, 4097], 16, [1, 5, 2, 7], "causal", 50, 256),
+    (2, 32, 2, 128, [300, 5000], 32, [8, 3], "causal", -1, 64),   # 2 row tiles
+    (2, 64, 1, 128, [200, 77], 16, [3, 1], "dense", -1, 256),     # G=64
+    (3, 16, 4, 256, [5, 129, 700], 8, [5, 1, 4], "causal", 0, 16),  # qlen == L
+]
+
+
+@pytest.mark.parametrize("i", range(len(DECODE_Q_SWEEP)))
+def test_decode_q_sweep(i):
+    B, Hq, Hkv, D, sl, ps, sq, mask, w, ncu = DECODE_Q_SWEEP[i]
+    _say("decode_q_sweep", DECODE_Q_SWEEP[i])
+    fixed = isinstance(sq, int)
+    case = W.make_decode_q(700 + i, B, Hq, Hkv, D, sl, ps, seq_len_q=sq if fixed else None,
+                           qlens=None if fixed else sq, mask=mask, window_left=w, extra_pages=2)
+    out, lse, S = run_decode_q(case, num_cus=ncu)
+    ref_o, ref_l = oracle_decode_q(case)
+    assert_close(f64(out), ref_o, TOL_BF16, f"out (splits={S})")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, _, _ = run_decode_q(case, out_dtype=torch.float32, num_cus=ncu)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
