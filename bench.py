@@ -58,11 +58,12 @@ def _sha256(paths):
     return h.hexdigest()
 
 
-def measured_traffic(kernels):
-    """HBM bytes per launch of the named kernels, from the counter runs recorded
-    in profiles/hbm_traffic.md (FETCH_SIZE and WRITE_SIZE per dispatch, each
-    scaled by what the same counter reads for a plain copy of known size).
-    None when a kernel has no record or its source changed since the record."""
+def measured_traffic(kernels, workload):
+    """HBM bytes per launch of the named kernels on one workload, from the counter
+    runs recorded in profiles/hbm_traffic.md (FETCH_SIZE and WRITE_SIZE per
+    dispatch, each scaled by what the same counter reads for a plain copy of
+    known size).  None when a kernel has no record for the workload or its
+    source changed since the record was taken."""
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
     except OSError:
@@ -72,10 +73,10 @@ def measured_traffic(kernels):
         if not ln.startswith("traffic-record:"):
             continue
         f = dict(kv.split("=", 1) for kv in ln.split()[1:])
-        recs[f["kernel"]] = f
+        recs[(f["kernel"], f["workload"])] = f
     total = 0
     for k in kernels:
-        r = recs.get(k)
+        r = recs.get((k, workload))
         if r is None or _sha256([os.path.join(ROOT, x) for x in r["source"].split(",")]) != r["sha256"]:
             return None
         total += int(r["bytes_per_launch"])
@@ -189,10 +190,44 @@ def bench_decode(steps, warmup, W, P):
            "kv_bytes_per_step": kv_bytes}
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(["decode_kernel<128>", "decode_merge_kernel<128>"]),
+            "traffic": measured_traffic(["decode_kernel<128>", "decode_merge_kernel<128>"], "decode"),
             "kernel": "decode_kernel<128> + decode_merge_kernel<128> (one step)",
             "per_unit": "4096 B of K+V per live token (Hkv=8, D=128, bf16)"}
     return case, gbs, ms_step, cfg, roof
+
+
+def bench_decode_q(steps, warmup, W, P, SQ=4):
+    log(f"decode_q: generating inputs (SQ={SQ})")
+    case = W.batch_decode_q(SQ=SQ)
+    B, _, Hq, D = case.q.shape
+    Hkv, ps = case.k.shape[1], case.k.shape[2]
+    q = case.q.cuda()
+    k = case.k.cuda()
+    v = case.v.cuda()
+    ip, ix, sl = dev_i32(case.kv_indptr), dev_i32(case.kv_indices), dev_i32(case.seq_lens)
+    nbytes, S, split_len = P.paged_decode_q_workspace_size(B, SQ, Hq, Hkv, D, case.max_seq_len, ps)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(B, SQ, Hq, dtype=torch.float32, device="cuda")
+    P.paged_decode_q_validate(B, k.shape[0], ps, case.max_seq_len, case.kv_indptr,
+                              case.kv_indices, case.seq_lens, seq_len_q=SQ)
+
+    def step():
+        P.paged_decode_q_run(q, (k, v), ip, ix, sl, case.max_seq_len, ws, mask_type="causal",
+                             out=out, lse=lse)
+
+    ms_step, ms_launch = time_launches(step, steps, warmup)
+    kv_bytes = int(case.seq_lens.astype(np.int64).sum()) * Hkv * D * 2 * 2
+    return {"workload": f"multi-token paged decode B=64 SQ={SQ} Hq=32 Hkv=8 D=128 causal "
+                        "seq_lens~U[512,8192] page_size=16 bf16 (seed 2)",
+            "metric": "decode KV-read GB/s", "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "ms_per_step": round(ms_step, 4), "num_splits": S,
+            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "achieved": round(kv_bytes / (ms_launch * 1e-3) / 1e9, 1),
+                         "frac": round(kv_bytes / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(["attn_fwd_kernel<128,4,decode>",
+                                                      "decode_merge_kernel<128>"], "decode_q"),
+                         "kernel": "attn_fwd_kernel<128,4,decode> + decode_merge_kernel<128>"}}
 
 
 def bench_bsa_long(steps, warmup, W, P):
@@ -224,7 +259,7 @@ def bench_bsa_long(steps, warmup, W, P):
             "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(["attn_fwd_kernel<128,8,bsa>"]),
+                         "traffic": measured_traffic(["attn_fwd_kernel<128,8,bsa>"], "bsa"),
                          "kernel": "attn_fwd_kernel<128,%d,bsa>" % wr.plan.waves}}
 
 
@@ -255,7 +290,8 @@ def bench_prefill(steps, warmup, W, P, D=128, window_left=-1):
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic(
-                             ["attn_fwd_kernel<%d,%d,prefill>" % (D, wr.plan.waves)]),
+                             ["attn_fwd_kernel<%d,%d,prefill>" % (D, wr.plan.waves)],
+                             "prefill_d%d_w%d" % (D, window_left)),
                          "kernel": "attn_fwd_kernel<%d,%d,prefill>" % (D, wr.plan.waves)}}
 
 
@@ -331,7 +367,7 @@ def bench_sage(steps, warmup, W, P):
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4),
                          "frac_of_bf16_peak": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(["sage_kernel"]), "kernel": "sage_kernel"}}
+                         "traffic": measured_traffic(["sage_kernel"], "sage"), "kernel": "sage_kernel"}}
 
 
 def bench_copy():
@@ -379,8 +415,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["decode", "bsa", "prefill", "prefill256", "tiny", "sage",
-                                       "copy"], default=None,
+    ap.add_argument("--only", choices=["decode", "decode_q", "bsa", "prefill", "prefill256", "tiny",
+                                       "sage", "copy"], default=None,
                     help="run one workload only (for profiling; copy = counter calibration)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -400,6 +436,7 @@ def main(argv=None):
               "prefill256": lambda: bench_prefill(a.steps, a.warmup, W, P, D=256),
               "tiny": lambda: bench_bsa_tiny(a.steps, a.warmup, W, P),
               "sage": lambda: bench_sage(a.steps, a.warmup, W, P),
+              "decode_q": lambda: bench_decode_q(a.steps, a.warmup, W, P),
               "copy": bench_copy}[a.only]
         print(json.dumps(fn()), flush=True)
         return 0
@@ -413,6 +450,7 @@ def main(argv=None):
                    lambda: bench_prefill(a.steps, a.warmup, W, P, window_left=1024),
                    lambda: bench_prefill(a.steps, a.warmup, W, P, D=256),
                    lambda: bench_sage(a.steps, a.warmup, W, P),
+                   lambda: bench_decode_q(a.steps, a.warmup, W, P),
                    lambda: bench_bsa_tiny(a.steps, a.warmup, W, P)):
             r = fn()
             log(f"{r['workload']}: {r['value']} {r['unit']}")

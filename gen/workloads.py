@@ -366,6 +366,19 @@ def batch_decode(seed=2, B=64, Hq=32, Hkv=8, D=128, lo=512, hi=8192, page_size=1
                       "dense", -1, None, 1.0, "batch_decode")
 
 
+def batch_decode_q(seed=2, B=64, SQ=4, Hq=32, Hkv=8, D=128, lo=512, hi=8192, page_size=16):
+    """Multi-token decode (speculative verification): the batch_decode recipe with
+    SQ query tokens per request at the last SQ positions, causal mask."""
+    rng = _rng(seed)
+    seq_lens = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+    q = randn_bf16(rng, (B, SQ, Hq, D))
+    indptr, indices, P = csr_page_table(rng, seq_lens, page_size)
+    k = randn_bf16(rng, (P, Hkv, page_size, D))
+    v = randn_bf16(rng, (P, Hkv, page_size, D))
+    return DecodeQCase(q, k, v, indptr, indices, seq_lens, None, SQ, int(seq_lens.max()),
+                       "causal", -1, f"batch_decode_q{SQ}")
+
+
 def batch_prefill(seed=3, D=128, window_left=-1, B=8, Hq=32, Hkv=8, page_size=32,
                   qlo=256, qhi=2048, plo=0, phi=2048):
     """B=8 packed causal prefill, qlen ~ U{256..2048}, KV = qlen + U{0..2048}
