@@ -8,7 +8,7 @@
  *      signature and Parameters)                         -> bsa_plan / bsa_validate / bsa_run
  *   - packed-Q paged prefill
  *     (page "flashinfer.attention.prims_ts.batch_prefill_with_paged_kv_cache")
- *                                                        -> paged_prefill_validate / _plan / _run
+ *                                                        -> paged_prefill_validate / _plan / _plan_capacity / _run
  *   - single-token paged decode with caller scratch
  *     (page "flashinfer.attention.prims_ts.prims_ts_batch_decode_with_kv_cache")
  *                                                        -> paged_decode_validate / _workspace_size / _run
@@ -237,6 +237,23 @@ int paged_prefill_validate(const prefill_static_args* args, const int32_t* qo_in
 int paged_prefill_plan(const prefill_static_args* args, const int32_t* qo_indptr_h,
                        const int32_t* seq_lens_kv_h, pkb_prefill_plan_t* plan,
                        int32_t* worklist_h, int64_t worklist_cap, int64_t* n_work);
+
+/* Capacity plan for graph capture (prefill page, description: planning happens
+ * outside a captured graph and replays only launch).  No request metadata is
+ * read: the work list covers every request holding up to max_qlen query
+ * rows, so one captured paged_prefill_run stays correct while qo_indptr /
+ * seq_lens / block_tables change between replays within these bounds: every
+ * qlen in [1, max_qlen],
+ * qo_indptr starting at 0 and strictly increasing with qo_indptr[B] <= total_q
+ * (rows past qo_indptr[B] of out / lse are not written), and the rest of the
+ * paged_prefill_validate contract.  Tiles with no live rows exit at once.
+ * Items: n_work = B * ceil(max_qlen * group / tile_m), ordered by tile index
+ * from last to first and by request within a tile index; kv_tokens = 0.
+ * max_qlen outside [1, total_q] -> PKB_ERR_ARG; worklist_cap < n_work (or a
+ * NULL worklist_h) -> PKB_ERR_WORKSPACE with *n_work set. */
+int paged_prefill_plan_capacity(const prefill_static_args* args, int32_t max_qlen,
+                                pkb_prefill_plan_t* plan, int32_t* worklist_h,
+                                int64_t worklist_cap, int64_t* n_work);
 
 /* Trusted run.  worklist_d: device copy of the plan's work list.  output_scale
  * multiplies the normalised output; out dtype from the plan. */

@@ -264,6 +264,30 @@ def prefill_plan(args, qo_indptr, seq_lens):
     return PKB_OK, plan, wl
 
 
+def prefill_plan_capacity(args, max_qlen):
+    """Capacity work list for graph capture: every request may own up to
+    max_qlen rows; tile indices from last to first, requests in order within
+    one.  Returns (status, plan dict, worklist [n, 2] int32)."""
+    st = prefill_check_static(**{k: args[k] for k in (
+        "B", "Hq", "Hkv", "D", "num_pages", "page_size", "total_q", "width", "mask_type",
+        "window_left", "qkv_dtype", "out_dtype", "num_cus")})
+    if st != PKB_OK:
+        return st, None, None
+    if not (1 <= max_qlen <= args["total_q"]):
+        return PKB_ERR_ARG, None, None
+    B, Hq, Hkv = args["B"], args["Hq"], args["Hkv"]
+    G = Hq // Hkv
+    waves = prefill_waves(args)
+    tile_m = 32 * waves
+    T = cdiv(max_qlen * G, tile_m)
+    wl = np.array([[b, t * tile_m] for t in range(T - 1, -1, -1) for b in range(B)],
+                  dtype=np.int32).reshape(-1, 2)
+    plan = dict(group=G, waves=waves, tile_m=tile_m, n_work=len(wl), grid_x=len(wl),
+                grid_y=Hkv, kernel_id=kernel_id(args["D"], waves, args["out_dtype"]),
+                kv_tokens=0)
+    return PKB_OK, plan, wl
+
+
 # ----------------------------------------------------------------------------
 # Decode
 # ----------------------------------------------------------------------------

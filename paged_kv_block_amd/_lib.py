@@ -75,6 +75,9 @@ _SIGS = {
                                        c_int64, POINTER(Bad)]),
     "paged_prefill_plan": (c_int, [POINTER(PrefillStaticArgs), c_void_p, c_void_p,
                                    POINTER(PrefillPlan), c_void_p, c_int64, POINTER(c_int64)]),
+    "paged_prefill_plan_capacity": (c_int, [POINTER(PrefillStaticArgs), c_int32,
+                                            POINTER(PrefillPlan), c_void_p, c_int64,
+                                            POINTER(c_int64)]),
     "paged_prefill_run": (c_int, [POINTER(PrefillPlan), c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_int64, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
                                   c_float, c_float, c_void_p, c_void_p, c_void_p]),

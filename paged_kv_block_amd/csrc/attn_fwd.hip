@@ -47,6 +47,8 @@
 //     returns a 4-key x 16-dim block of the row-major V tile column-wise; lane
 //     half h then holds keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key step --
 //     exactly the keys its S^T accumulator holds, so P^T feeds the MFMA as is.
+#include <atomic>
+
 #include "device_common.h"
 #include "pkb_internal.h"
 
@@ -665,14 +667,28 @@ static hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t st) {
   const size_t lds = AttnLayout<D, NW>::LDS;
   const void* kern = p.out_f32 ? (const void*)attn_fwd_kernel<D, NW, MODE, true, true>
                                : (const void*)attn_fwd_kernel<D, NW, MODE, false, true>;
+  int variant = p.out_f32 ? 1 : 0;
   if constexpr (MODE == kModeBsa) {
-    if (p.kvbs % 64 != 0)   // sparse blocks of 8, 16 or 32 keys: several per tile
+    if (p.kvbs % 64 != 0) {   // sparse blocks of 8, 16 or 32 keys: several per tile
       kern = p.out_f32 ? (const void*)attn_fwd_kernel<D, NW, MODE, true, false>
                        : (const void*)attn_fwd_kernel<D, NW, MODE, false, false>;
+      variant += 2;
+    }
   }
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // The LDS limit is an attribute of the function on one device: raise it on
+    // the first launch there only, so later launches (and graph capture) make
+    // no extra runtime calls.
+    static std::atomic<uint64_t> raised[4];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+    if (!(raised[variant].load(std::memory_order_acquire) & bit)) {
+      e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      raised[variant].fetch_or(bit, std::memory_order_release);
+    }
   }
   AttnParams arg = p;
   void* args[] = {(void*)&arg};

@@ -270,6 +270,42 @@ int paged_prefill_plan(const prefill_static_args* a, const int32_t* qo_indptr,
   return PKB_OK;
 }
 
+int paged_prefill_plan_capacity(const prefill_static_args* a, int32_t max_qlen,
+                                pkb_prefill_plan_t* plan, int32_t* worklist,
+                                int64_t worklist_cap, int64_t* n_work) {
+  int st = prefill_static_check(a);
+  if (st) return st;
+  if (!plan || max_qlen < 1 || max_qlen > a->total_q) return PKB_ERR_ARG;
+  const int G = a->Hq / a->Hkv;
+  const int waves = a->D == 128 ? 8 : 4;
+  const int tile_m = 32 * waves;
+  // every request may own up to max_qlen rows: ceil(max_qlen * G / tile_m) tiles
+  // each, latest tiles first (under bottom-right causal alignment they admit
+  // the most keys), requests in order within a tile index
+  const int64_t T = cdiv((int64_t)max_qlen * G, tile_m);
+  const int64_t n = T * a->B;
+  if (n_work) *n_work = n;
+  memset(plan, 0, sizeof(*plan));
+  plan->a = *a;
+  plan->group = G;
+  plan->waves = waves;
+  plan->tile_m = tile_m;
+  plan->n_work = (int32_t)std::min<int64_t>(n, 0x7fffffff);
+  plan->grid_x = plan->n_work;
+  plan->grid_y = a->Hkv;
+  plan->kernel_id = kernel_id(a->D, waves, a->out_dtype);
+  plan->kv_tokens = 0;
+  if (n > 0x7fffffff) return PKB_ERR_UNSUPPORTED;
+  if (worklist_cap < n || !worklist) return PKB_ERR_WORKSPACE;
+  int64_t i = 0;
+  for (int64_t t = T - 1; t >= 0; --t)
+    for (int b = 0; b < a->B; ++b, ++i) {
+      worklist[2 * i] = b;
+      worklist[2 * i + 1] = (int32_t)(t * tile_m);
+    }
+  return PKB_OK;
+}
+
 // ------------------------------------------------------------------ decode
 
 int paged_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,

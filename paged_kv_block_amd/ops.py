@@ -221,6 +221,21 @@ def paged_prefill_plan(args: PrefillStaticArgs, qo_indptr, seq_lens_kv):
     return plan, wl[:n.value]
 
 
+def paged_prefill_plan_capacity(args: PrefillStaticArgs, max_qlen):
+    """Capacity plan (reads no request metadata): (plan, worklist int32 [n_work, 2])."""
+    plan = PrefillPlan()
+    n = ctypes.c_int64(0)
+    st = lib().paged_prefill_plan_capacity(ctypes.byref(args), int(max_qlen), ctypes.byref(plan),
+                                           None, 0, ctypes.byref(n))
+    if st != C.PKB_ERR_WORKSPACE:
+        check(st, "paged_prefill_plan_capacity")
+    wl = np.zeros((n.value, 2), dtype=np.int32)
+    check(lib().paged_prefill_plan_capacity(ctypes.byref(args), int(max_qlen), ctypes.byref(plan),
+                                            _hp(wl), n.value, ctypes.byref(n)),
+          "paged_prefill_plan_capacity")
+    return plan, wl
+
+
 def paged_prefill_run(plan: PrefillPlan, worklist_d, q, k_cache, v_cache, qo_indptr,
                       block_tables, seq_lens_kv, sm_scale=None, output_scale=1.0, out=None,
                       lse=None, stream=None):
@@ -251,6 +266,23 @@ class BatchPrefillPagedWrapper:
         dev = device if device is not None else torch.device("cuda")
         self.worklist = torch.from_numpy(wl.copy()).to(dev)
         self.out_dtype = out_dtype
+
+    @classmethod
+    def for_capacity(cls, B, max_qlen, total_q, Hq, Hkv, D, num_pages, page_size,
+                     block_table_width, mask_type="dense", window_left=-1,
+                     out_dtype=torch.bfloat16, device=None):
+        """Plan from static bounds only, for a ``run`` captured once in a graph and
+        replayed while qo_indptr / seq_lens / block_tables change (every qlen at
+        most max_qlen, qo_indptr[B] at most total_q)."""
+        self = cls.__new__(cls)
+        self.args = _prefill_args(B, Hq, Hkv, D, num_pages, page_size, total_q,
+                                  block_table_width, mask_type, window_left, out_dtype,
+                                  num_cus(device))
+        self.plan, wl = paged_prefill_plan_capacity(self.args, max_qlen)
+        dev = device if device is not None else torch.device("cuda")
+        self.worklist = torch.from_numpy(wl.copy()).to(dev)
+        self.out_dtype = out_dtype
+        return self
 
     def run(self, q, k_cache, v_cache, qo_indptr, block_tables, seq_lens_kv, sm_scale=None,
             output_scale=1.0, out=None, lse=None):

@@ -218,6 +218,28 @@ def test_prefill_worklist_matches_spec(mask, w):
             assert getattr(plan_c, k) == v, k
 
 
+@pytest.mark.parametrize("D,mq", [(128, 1), (128, 300), (256, 2048), (128, 65)])
+def test_prefill_capacity_plan_matches_spec(D, mq):
+    args = _prefill_args(5, 4000, 64, 1, -1, D=D, num_pages=100)
+    st, plan_py, wl_py = M.prefill_plan_capacity(args, mq)
+    assert st == 0
+    a = C.PrefillStaticArgs(*[args[k] for k in ("B", "Hq", "Hkv", "D", "num_pages", "page_size",
+                                                "total_q", "width", "mask_type", "window_left",
+                                                "qkv_dtype", "out_dtype", "num_cus")])
+    plan_c, wl_c = P.paged_prefill_plan_capacity(a, mq)
+    assert np.array_equal(wl_c, wl_py)
+    for k, v in plan_py.items():
+        assert getattr(plan_c, k) == v, k
+    # every (request, tile) that any qlen <= mq can need appears exactly once
+    G, tm = plan_py["group"], plan_py["tile_m"]
+    need = {(b, r) for b in range(5) for r in range(0, mq * G, tm)}
+    assert sorted(map(tuple, wl_py.tolist())) == sorted(need)
+    for bad_q in (0, 4001):
+        assert M.prefill_plan_capacity(args, bad_q)[0] == M.PKB_ERR_ARG
+        with pytest.raises(P.PkbError):
+            P.paged_prefill_plan_capacity(a, bad_q)
+
+
 def _c_prefill_validate(args, qo, sl, bt):
     a = C.PrefillStaticArgs(args["B"], args["Hq"], args["Hkv"], args["D"], args["num_pages"],
                             args["page_size"], args["total_q"], args["width"], args["mask_type"],
