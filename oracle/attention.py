@@ -344,15 +344,19 @@ def sage_block_size(block_sizes, b, h, beta):
 def sage_reference(q_int8, k_int8, v_fp8_codes, q_scale, k_scale, v_scale,
                    q2k_block_index, block_sparse_num, block_sizes=None,
                    q2k_block_nums=None, uniform_block_count=False, softmax_scale=None,
-                   Sk=None, rows=None):
+                   Sk=None, rows=None, mask="dense", with_lse=False):
     """Sage block-sparse attention on the dequantised inputs (MHA, D=128,
-    64-token blocks, no mask inside blocks).
+    64-token blocks).
 
     Query block r = i // 64 uses n = q2k_block_nums[b,h,r] when counts are given
     and ``uniform_block_count`` is false, else ``block_sparse_num``; it selects
     blocks q2k_block_index[b,h,r,:n].  Block beta admits its first
-    block_sizes[..beta] tokens, clipped to Sk.  rows: optional list of
-    (b, h, r) query blocks.  Returns out [B, H, Sq, 128] (NaN outside ``rows``).
+    block_sizes[..beta] tokens, clipped to Sk.  With mask="causal" (the
+    token-level causal rule of the block-sparse page, bottom-right aligned:
+    query i sits at position Sk - Sq + i) a selected token j is admitted only
+    when j <= Sk - Sq + i.  rows: optional list of (b, h, r) query blocks.
+    Returns out [B, H, Sq, 128] (NaN outside ``rows``) and, with ``with_lse``,
+    the natural-log LSE [B, H, Sq] of the scaled scores (-inf for empty rows).
     """
     Qd, Kd, Vd = sage_dequantize(q_int8, k_int8, v_fp8_codes, q_scale, k_scale, v_scale, Sk)
     B, H, Sq, D = Qd.shape
@@ -364,8 +368,10 @@ def sage_reference(q_int8, k_int8, v_fp8_codes, q_scale, k_scale, v_scale,
     if rows is None:
         rows = [(b, h, r) for b in range(B) for h in range(H) for r in range(nqb)]
         out = np.zeros((B, H, Sq, D))
+        lse = np.full((B, H, Sq), -np.inf)
     else:
         out = np.full((B, H, Sq, D), np.nan)
+        lse = np.full((B, H, Sq), np.nan)
     for b, h, r in rows:
         n = int(nums[b, h, r]) if (nums is not None and not uniform_block_count) \
             else int(block_sparse_num)
@@ -376,7 +382,9 @@ def sage_reference(q_int8, k_int8, v_fp8_codes, q_scale, k_scale, v_scale,
             toks.append(t[t < Sk])
         j = np.concatenate(toks) if toks else np.zeros(0, dtype=np.int64)
         i0, i1 = r * 64, min(r * 64 + 64, Sq)
-        adm = np.ones((i1 - i0, j.size), dtype=bool)
-        o, _ = attend(Qd[b, h, i0:i1], Kd[b, h, j], Vd[b, h, j], adm, scale)
+        p = Sk - Sq + np.arange(i0, i1)
+        adm = position_mask(p, j, mask == "causal", -1)
+        o, s = attend(Qd[b, h, i0:i1], Kd[b, h, j], Vd[b, h, j], adm, scale)
         out[b, h, i0:i1] = o
-    return out
+        lse[b, h, i0:i1] = s
+    return (out, lse) if with_lse else out

@@ -403,6 +403,60 @@ def test_sage_all_blocks_equals_dense_sdpa():
     cmp(out, ref, 1e-12)
 
 
+@pytest.mark.parametrize("Sq,Sk", [(150, 150), (100, 180)])
+def test_sage_causal_all_blocks_equals_masked_sdpa(Sq, Sk):
+    """Causal Sage with every block selected is dense SDPA with the bottom-right
+    causal mask on the dequantised tensors (torch fp64, explicit boolean mask),
+    and its LSE normalises the softmax weights of the admitted keys."""
+    case = W.make_sage(33, 1, 2, Sq, Sk, cap=3, nsel=3, per_row_counts=False,
+                       block_sizes_rank=0)
+    nkb = -(-Sk // 64)
+    idx = np.tile(np.arange(nkb, dtype=np.int32), (1, 2, -(-Sq // 64), 1))
+    codes = case.v_fp8.view(torch.uint8).numpy()
+    out, lse = A.sage_reference(case.q_int8, case.k_int8, codes, case.q_scale, case.k_scale,
+                                case.v_scale, idx, nkb, Sk=Sk, mask="causal", with_lse=True)
+    Qd, Kd, Vd = A.sage_dequantize(case.q_int8, case.k_int8, codes, case.q_scale,
+                                   case.k_scale, case.v_scale, Sk)
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    m = torch.from_numpy(j <= Sk - Sq + i)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Qd), torch.from_numpy(Kd), torch.from_numpy(Vd), attn_mask=m,
+        scale=1 / math.sqrt(128)).numpy()
+    cmp(out, ref, 1e-12)
+    s = np.einsum("bhid,bhjd->bhij", Qd, Kd) / math.sqrt(128)
+    w = np.where(m.numpy()[None, None], np.exp(s - lse[..., None]), 0.0)
+    cmp(w.sum(-1), np.ones_like(lse), 1e-12)
+    # the first query of a square problem sees key 0 only: out = V[0], LSE = s[0, 0]
+    if Sq == Sk:
+        cmp(out[:, :, 0], Vd[:, :, 0], 1e-12)
+        cmp(lse[:, :, 0], s[:, :, 0, 0], 1e-12)
+
+
+def test_sage_dense_lse_matches_logsumexp_of_selected_keys():
+    """Dense Sage LSE of one query block equals scipy's logsumexp over exactly the
+    selected keys (block order permuted, one partial block)."""
+    from scipy.special import logsumexp
+    case = W.sage_small(34, block_sizes_rank=1)
+    codes = case.v_fp8.view(torch.uint8).numpy()
+    out, lse = A.sage_reference(case.q_int8, case.k_int8, codes, case.q_scale, case.k_scale,
+                                case.v_scale, case.q2k_block_index, case.block_sparse_num,
+                                case.block_sizes, case.q2k_block_nums, False, None, Sk=case.Sk,
+                                with_lse=True)
+    Qd, Kd, _ = A.sage_dequantize(case.q_int8, case.k_int8, codes, case.q_scale, case.k_scale,
+                                  case.v_scale, case.Sk)
+    for b, h, r in [(0, 0, 0), (1, 2, 15), (0, 1, 7)]:
+        n = int(case.q2k_block_nums[b, h, r])
+        toks = [t for beta in case.q2k_block_index[b, h, r, :n]
+                for t in range(beta * 64, beta * 64 + int(case.block_sizes[beta])) if t < case.Sk]
+        for i in range(r * 64, min(r * 64 + 64, 1000), 13):
+            if not toks:
+                assert lse[b, h, i] == -np.inf
+                continue
+            sc = np.array([Qd[b, h, i] @ Kd[b, h, t] for t in toks]) / math.sqrt(128)
+            cmp(lse[b, h, i], logsumexp(sc), 1e-12)
+
+
 def test_sage_dequant_groups():
     """One q scale per 32 rows (ceil(Sq/128)*4 entries) and one k scale per 64
     rows: a constructed case with distinct per-group scales."""
