@@ -365,7 +365,7 @@ int bsa_sage_validate(const int32_t* q2k_block_index_h, int32_t capacity,
                       int32_t uniform_block_count, int32_t B, int32_t H, int32_t Sq,
                       int32_t Sk, pkb_bad_t* bad);
 
-/* Trusted run (MHA, D = 128, 64-token blocks, no mask inside blocks, no LSE).
+/* Trusted run (MHA, D = 128, 64-token blocks).
  *   q [B,H,Sq,128] int8, k [B,H,Sk,128] int8,
  *   v_fp8 [B,H,128,ceil(Sk/64)*64] OCP E4M3FN in HDS layout (tokens contiguous),
  *   q_scale [B,H,ceil(Sq/128)*4] (one per 32 rows), k_scale [B,H,ceil(Sk/64)],
@@ -375,9 +375,17 @@ int bsa_sage_validate(const int32_t* q2k_block_index_h, int32_t capacity,
  *   uniform_block_count == 0, else every row uses block_sparse_num;
  *   block_sizes (NULL = 64) of rank 1 [nkb], 2 [B,nkb] or 3 [B,H,nkb]:
  *   valid-token count of each KV block (its first tokens);
- *   contiguous_block_indices: accepted, needs uniform_block_count, otherwise
- *   ignored;  softmax_scale <= 0 selects 1/sqrt(128);
- *   out [B,H,Sq,128] bf16.  A row selecting zero blocks is written as zeros. */
+ *   contiguous_block_indices (needs uniform_block_count, else PKB_ERR_ARG):
+ *   the caller promises that each row's blocks are index[0], index[0] + 1, ...;
+ *   only index[0] is read (Parameters: the promise is trusted, not checked).
+ *   Block ids outside [0, ceil(Sk/64)) then count as empty blocks;
+ *   softmax_scale <= 0 selects 1/sqrt(128);
+ *   mask_type: PKB_MASK_DENSE as on the page, or PKB_MASK_CAUSAL, an addition
+ *   that applies the block-sparse page's token-level causal rule to the
+ *   selected tokens (query i at position Sk - Sq + i admits tokens j <= that);
+ *   out [B,H,Sq,128] bf16; lse [B,H,Sq] fp32 natural-log LSE or NULL (an
+ *   addition: the page's kernel returns no LSE).  A row with no admitted
+ *   token is written as zeros (LSE -inf). */
 int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
                  const float* q_scale, const float* k_scale, const float* v_scale,
                  const int32_t* q2k_block_index, int32_t capacity,
@@ -385,7 +393,7 @@ int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
                  int32_t block_sizes_rank, const int32_t* q2k_block_nums,
                  int32_t uniform_block_count, int32_t contiguous_block_indices,
                  int32_t B, int32_t H, int32_t Sq, int32_t Sk, float softmax_scale,
-                 void* out, void* stream);
+                 int32_t mask_type, void* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -105,8 +105,8 @@ _SIGS = {
                                   c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(Bad)]),
     "bsa_sage_run": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int32,
-                             c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_void_p,
-                             c_void_p]),
+                             c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_int32,
+                             c_void_p, c_void_p, c_void_p]),
 }
 
 EXPORTS = tuple(_SIGS)

@@ -330,8 +330,9 @@ int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
                  const int32_t* block_sizes, int32_t block_sizes_rank,
                  const int32_t* q2k_block_nums, int32_t uniform_block_count,
                  int32_t contiguous_block_indices, int32_t B, int32_t H, int32_t Sq, int32_t Sk,
-                 float softmax_scale, void* out, void* stream) {
+                 float softmax_scale, int32_t mask_type, void* out, float* lse, void* stream) {
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || capacity < 0) return PKB_ERR_ARG;
+  if (mask_type != PKB_MASK_DENSE && mask_type != PKB_MASK_CAUSAL) return PKB_ERR_ARG;
   if (block_sparse_num < 0 || block_sparse_num > capacity) return PKB_ERR_ARG;
   if (contiguous_block_indices && !uniform_block_count) return PKB_ERR_ARG;
   if (block_sizes && (block_sizes_rank < 1 || block_sizes_rank > 3)) return PKB_ERR_ARG;
@@ -352,6 +353,9 @@ int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
   p.nums = uniform_block_count ? nullptr : q2k_block_nums;
   p.block_sizes = block_sizes;
   p.out = (uint16_t*)out;
+  p.lse = lse;
+  p.causal = mask_type == PKB_MASK_CAUSAL;
+  p.contig = contiguous_block_indices != 0;
   p.B = B;
   p.H = H;
   p.Sq = Sq;

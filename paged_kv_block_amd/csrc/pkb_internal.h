@@ -85,8 +85,11 @@ struct SageParams {
   const int32_t* nums;        // null => block_sparse_num
   const int32_t* block_sizes; // null => 64
   uint16_t* out;
+  float* lse;                 // null => no LSE output; else [B, H, Sq] natural log
   int B, H, Sq, Sk, Skp, nqb, nkb, capacity, block_sparse_num;
   int bs_rank, qs_len;
+  int causal;                 // token-level causal, query i at position Sk - Sq + i
+  int contig;                 // selected blocks are idx[0], idx[0] + 1, ... (trusted)
   float scale_log2;
 };
 

@@ -8,7 +8,12 @@
 // its first block_sizes[..beta] tokens (< Sk):
 //     s_j = softmax_scale * (q_int8[i] . k_int8[j]) * q_scale[i/32] * k_scale[j/64]
 //     out[i, d] = sum_j softmax(s)_j * e4m3(v[d, j]) * v_scale[d]    (bf16)
-// A row with no selected block is written as zeros.
+// A row with no selected block is written as zeros.  Two additions beyond the
+// page: an optional token-level causal mask (the block-sparse page's rule,
+// bottom-right aligned: query i at position Sk - Sq + i) and an optional LSE
+// output (natural log of the sum of exp(s_j) over admitted keys).  With
+// contiguous selections (the page's contiguous_block_indices promise) block t
+// is the first selected index plus t.
 //
 // One workgroup = (b, h, query block of 64 rows): two waves of 32 rows.  Per
 // selected KV block (64 tokens, one tile):
@@ -101,16 +106,25 @@ sage_kernel(const SageParams p) {
 
   const int32_t* idx = p.index + (bh * p.nqb + r) * p.capacity;
   const int n = p.nums ? ld_const(p.nums, bh * p.nqb + r) : p.block_sparse_num;
+  // contiguous selections: block t is the first index + t (no index loads)
+  const int beta0 = (p.contig && n > 0) ? ld_const(idx, 0) : 0;
 
   const int row = r * 64 + wave * 32 + ql;
   const bool row_ok = row < p.Sq;
+  // causal: row i sits at position Sk - Sq + i; a block starting past the
+  // workgroup's last position admits nothing
+  const int p_row = p.Sk - p.Sq + row;
+  const int p_last = p.Sk - p.Sq + min(r * 64 + 63, p.Sq - 1);
 
-  // block metadata: id and valid-token count (0: nothing to do)
+  // block metadata: id and valid-token count (0: nothing to do).  Ids outside
+  // [0, nkb) count as empty, so even a wrong contiguity promise stays in bounds.
   struct BlockMeta { int beta, kv; };
   auto block_meta = [&](int t) -> BlockMeta {
     BlockMeta m;
-    m.beta = ld_const(idx, t);
-    m.kv = min(sage_block_size(p, b, h, m.beta), p.Sk - m.beta * 64);
+    m.beta = p.contig ? beta0 + t : ld_const(idx, t);
+    m.kv = 0;
+    if ((unsigned)m.beta < (unsigned)p.nkb && !(p.causal && m.beta * 64 > p_last))
+      m.kv = min(sage_block_size(p, b, h, m.beta), p.Sk - m.beta * 64);
     return m;
   };
   // this wave's share of block t's copies into ring stage t % kNStage: K rows
@@ -235,7 +249,8 @@ sage_kernel(const SageParams p) {
       // ---- scale, mask keys >= kv (element (kb, i) is key 32hh + 16kb + i) ----
       float sv[2][16];
       float mx = -INFINITY;
-      const int kvh = kv - 32 * hh;
+      int kvh = kv - 32 * hh;        // keys of this lane half below the block size
+      if (p.causal) kvh = min(kvh, p_row - bm[0].beta * 64 - 32 * hh + 1);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -300,6 +315,8 @@ sage_kernel(const SageParams p) {
   const float l_tot = half_sum(l_run);
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / (kP8 * l_tot) : 0.f;
+  if (p.lse && hh == 0)
+    p.lse[bh * p.Sq + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   const float* vsc = p.v_scale + bh * 128;
   uint16_t* o = p.out + (bh * p.Sq + row) * 128;
 #pragma unroll

@@ -492,7 +492,8 @@ def bsa_sage_validate(q2k_block_index, capacity, block_sparse_num, block_sizes, 
 
 def bsa_sage_run(q_int8, k_int8, v_fp8, q_scale, k_scale, v_scale, q2k_block_index,
                  block_sparse_num, block_sizes=None, q2k_block_nums=None, softmax_scale=None, *,
-                 out, uniform_block_count=False, contiguous_block_indices=False, stream=None):
+                 out, uniform_block_count=False, contiguous_block_indices=False,
+                 mask_type="dense", lse=None, stream=None):
     B, H, Sq, D = q_int8.shape
     Sk = k_int8.shape[2]
     _need(D == 128 and k_int8.shape[3] == 128, "head dim must be 128")
@@ -507,12 +508,16 @@ def bsa_sage_run(q_int8, k_int8, v_fp8, q_scale, k_scale, v_scale, q2k_block_ind
     for t in (q_int8, k_int8, v_fp8, q_scale, k_scale, v_scale, q2k_block_index, out):
         _need(t.is_cuda and t.is_contiguous(), "all Sage tensors must be contiguous CUDA tensors")
     _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (B, H, Sq, 128), "out must be bf16 BHSD")
+    if lse is not None:
+        _need(lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous()
+              and lse.numel() == B * H * Sq, "lse must be fp32 [B, H, Sq]")
     rank = 0 if block_sizes is None else block_sizes.dim()
     st = lib().bsa_sage_run(_ptr(q_int8), _ptr(k_int8), _ptr(v_fp8), _ptr(q_scale), _ptr(k_scale),
                             _ptr(v_scale), _ptr(q2k_block_index), cap, int(block_sparse_num),
                             _ptr(block_sizes), rank, _ptr(q2k_block_nums),
                             int(bool(uniform_block_count)), int(bool(contiguous_block_indices)),
-                            B, H, Sq, Sk, float(softmax_scale or 0.0), _ptr(out),
+                            B, H, Sq, Sk, float(softmax_scale or 0.0), _MASK[mask_type],
+                            _ptr(out), _ptr(lse),
                             stream if stream is not None else _stream(q_int8.device))
     check(st, "bsa_sage_run")
     return out
@@ -521,9 +526,11 @@ def bsa_sage_run(q_int8, k_int8, v_fp8, q_scale, k_scale, v_scale, q2k_block_ind
 def bsa_attn_blk64_sage_fwd(q_int8, k_int8, v_fp8, q_scale, k_scale, v_scale, q2k_block_index,
                             block_sparse_num, block_sizes=None, q2k_block_nums=None,
                             softmax_scale=None, *, out=None, uniform_block_count=False,
-                            contiguous_block_indices=False, validate=False):
+                            contiguous_block_indices=False, validate=False, mask_type="dense",
+                            lse=None):
     """Mirrors the page "bsa_attn_sm120_blk64_sage_fwd" (caller-owned ``out``;
-    allocated here when omitted)."""
+    allocated here when omitted).  ``mask_type="causal"`` and ``lse`` are
+    additions beyond the page."""
     B, H, Sq, _ = q_int8.shape
     Sk = k_int8.shape[2]
     if validate:
@@ -534,4 +541,5 @@ def bsa_attn_blk64_sage_fwd(q_int8, k_int8, v_fp8, q_scale, k_scale, v_scale, q2
     return bsa_sage_run(q_int8, k_int8, v_fp8, q_scale, k_scale, v_scale, q2k_block_index,
                         block_sparse_num, block_sizes, q2k_block_nums, softmax_scale, out=out,
                         uniform_block_count=uniform_block_count,
-                        contiguous_block_indices=contiguous_block_indices)
+                        contiguous_block_indices=contiguous_block_indices, mask_type=mask_type,
+                        lse=lse)
