@@ -176,6 +176,24 @@ class SageCase:
     name: str = ""
 
 
+@dataclass
+class QsaCase:
+    """Packed-query token-granular sparse attention inputs (non-paged K/V)."""
+    q: torch.Tensor                 # [T, Hq, D] bf16
+    k: torch.Tensor                 # [T, Hkv, D] bf16
+    v: torch.Tensor                 # [T, Hkv, D] bf16
+    sel_blocks: np.ndarray          # [T, NB] uint8, nonzero selects a global block
+    lo: np.ndarray                  # [T] int32 inclusive key bounds
+    hi: np.ndarray                  # [T] int32
+    blk_base: np.ndarray            # [T] int32 first global block of the token's sequence
+    tok_base: np.ndarray            # [T] int32 first global token of the token's sequence
+    block_first: np.ndarray         # [NB] int32 inclusive token span of each block
+    block_last: np.ndarray          # [NB] int32
+    seq_lens: np.ndarray            # [n_seq] packed sequence lengths
+    scale: float = 0.0625
+    name: str = ""
+
+
 # ----------------------------------------------------------------------------
 # Block-sparse selections
 # ----------------------------------------------------------------------------
@@ -328,6 +346,79 @@ def make_decode_q(seed, B, Hq, Hkv, D, seq_lens, page_size, seq_len_q=None, qlen
     v = randn_bf16(rng, (P, Hkv, page_size, D))
     return DecodeQCase(q, k, v, indptr, indices, seq_lens, qo, sq, int(seq_lens.max()), mask,
                        window_left, name)
+
+
+def qsa_partition(seq_lens, block_size=4):
+    """Packed partition: per token its sequence's first token and first global
+    block; per global block its inclusive token span.  Blocks are numbered
+    globally, restarting at each sequence boundary (a sequence of length L owns
+    ceil(L/4) blocks, the last one possibly partial)."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    T = int(seq_lens.sum())
+    tok_base = np.zeros(T, dtype=np.int32)
+    blk_base = np.zeros(T, dtype=np.int32)
+    first, last = [], []
+    t0 = nb0 = 0
+    for L in seq_lens:
+        L = int(L)
+        tok_base[t0:t0 + L] = t0
+        blk_base[t0:t0 + L] = nb0
+        for m in range(-(-L // block_size)):
+            first.append(t0 + block_size * m)
+            last.append(min(t0 + block_size * m + block_size - 1, t0 + L - 1))
+        nb0 += -(-L // block_size)
+        t0 += L
+    return tok_base, blk_base, np.asarray(first, np.int32), np.asarray(last, np.int32)
+
+
+def make_qsa(seed, seq_lens, Hq=12, Hkv=1, D=256, p_sel=0.3, mode="causal", window=-1,
+             force_diag=True, n_sel=None, empty_rows=0, junk_bits=0.0, name=""):
+    """Token-granular selections over packed sequences.
+
+    Each token selects blocks of its own sequence: with probability ``p_sel``
+    each, or (``n_sel``) a random set of up to n_sel of the blocks its bounds
+    reach; ``force_diag`` adds the block holding the token itself.  Bounds:
+    causal lo = sequence start (or t - window), hi = t; dense lo/hi = the whole
+    sequence.  ``empty_rows`` tokens get lo > hi; ``junk_bits`` sets random bits
+    on blocks outside the token's bounds (they must not matter)."""
+    rng = _rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    tok_base, blk_base, bfirst, blast = qsa_partition(seq_lens)
+    T, NB = int(seq_lens.sum()), bfirst.size
+    q = randn_bf16(rng, (T, Hq, D))
+    k = randn_bf16(rng, (T, Hkv, D))
+    v = randn_bf16(rng, (T, Hkv, D))
+    lo = np.zeros(T, np.int32)
+    hi = np.zeros(T, np.int32)
+    sel = np.zeros((T, NB), np.uint8)
+    for t in range(T):
+        s0 = int(tok_base[t])
+        send = s0 + int(seq_lens[np.searchsorted(np.cumsum(seq_lens), t, side="right")]) - 1
+        if mode == "causal":
+            lo[t] = s0 if window < 0 else max(s0, t - window)
+            hi[t] = t
+        else:
+            lo[t], hi[t] = s0, send
+        b0 = int(blk_base[t])
+        nb_lo = b0 + (int(lo[t]) - s0) // 4
+        nb_hi = b0 + (int(hi[t]) - s0) // 4
+        cand = np.arange(nb_lo, nb_hi + 1)
+        if n_sel is None:
+            pick = cand[rng.random(cand.size) < p_sel]
+        else:
+            pick = rng.permutation(cand)[:n_sel]
+        sel[t, pick] = 1
+        if force_diag:
+            sel[t, b0 + (t - s0) // 4] = 1
+        if junk_bits > 0:
+            other = np.ones(NB, bool)
+            other[cand] = False
+            sel[t, other & (rng.random(NB) < junk_bits)] = 1
+    if empty_rows:
+        for t in rng.choice(T, size=empty_rows, replace=False):
+            lo[t], hi[t] = hi[t] + 1, hi[t]
+    return QsaCase(q, k, v, sel, lo, hi, blk_base, tok_base, bfirst, blast,
+                   seq_lens.astype(np.int32), 1.0 / math.sqrt(D), name)
 
 
 # ----------------------------------------------------------------------------

@@ -388,3 +388,40 @@ def sage_reference(q_int8, k_int8, v_fp8_codes, q_scale, k_scale, v_scale,
         out[b, h, i0:i1] = o
         lse[b, h, i0:i1] = s
     return (out, lse) if with_lse else out
+
+
+# ----------------------------------------------------------------------------
+# Packed-query token-granular sparse attention (QSA)
+# ----------------------------------------------------------------------------
+
+def qsa_reference(q, k, v, sel_blocks, lo, hi, block_first, block_last, scale=None,
+                  tokens=None):
+    """Page "qsa_forward" (Parameters, Returns, Notes): query token t attends to
+    the key tokens j of every global block nb it selects (sel_blocks[t, nb] != 0,
+    block nb spanning block_first[nb] .. block_last[nb] inclusive) that also lie
+    in [lo[t], hi[t]] (inclusive); nothing else is added (no implicit causal
+    tail).  K/V are the packed token arrays [T, Hkv, D]; query head h reads KV
+    head h // (Hq / Hkv).  Empty rows: out 0, LSE -inf.  Returns out [T, Hq, D]
+    and lse [Hq, T] (the page's layout).  ``tokens``: optional subset of query
+    tokens (others NaN)."""
+    q = _f64(q); k = _f64(k); v = _f64(v)
+    sel = np.asarray(sel_blocks)
+    lo = _i64(lo); hi = _i64(hi)
+    bf = _i64(block_first); bl = _i64(block_last)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = _default_scale(scale, D)
+    fill = 0.0 if tokens is None else np.nan
+    out = np.full((T, Hq, D), fill)
+    lse = np.full((Hq, T), -np.inf if tokens is None else np.nan)
+    for t in (range(T) if tokens is None else tokens):
+        spans = [np.arange(bf[nb], bl[nb] + 1) for nb in np.nonzero(sel[t])[0]]
+        j = np.unique(np.concatenate(spans)) if spans else np.zeros(0, np.int64)
+        j = j[(j >= lo[t]) & (j <= hi[t])]
+        for g in range(Hkv):
+            o, s = attend(q[t, g * G:(g + 1) * G], k[j, g], v[j, g],
+                          np.ones((G, j.size), bool), sc)
+            out[t, g * G:(g + 1) * G] = o
+            lse[g * G:(g + 1) * G, t] = s
+    return out, lse

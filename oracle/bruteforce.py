@@ -182,3 +182,31 @@ def decode_q_bruteforce(q, k, v, kv_indptr, kv_indices, seq_lens, qo_indptr,
                 out[row][h], lse[row][h] = _row_softmax(q[row][h], keys, vals, scale,
                                                         bmm2_scale)
     return out, lse
+
+
+def qsa_bruteforce(q, k, v, sel_blocks, lo, hi, block_first, block_last, scale):
+    """Page "qsa_forward": loops over (token, head, block, key) -- tiny inputs only.
+    Returns (out [T][Hq][D], lse [Hq][T])."""
+    q, k, v = _lst(q), _lst(k), _lst(v)
+    sel, lo, hi = _lst(sel_blocks), _lst(lo), _lst(hi)
+    bf, bl = _lst(block_first), _lst(block_last)
+    T, Hq, D = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k[0])
+    G = Hq // Hkv
+    out = [[None] * Hq for _ in range(T)]
+    lse = [[None] * T for _ in range(Hq)]
+    for t in range(T):
+        keys = set()
+        for nb in range(len(bf)):
+            if sel[t][nb]:
+                for j in range(bf[nb], bl[nb] + 1):
+                    if lo[t] <= j <= hi[t]:
+                        keys.add(j)
+        keys = sorted(keys)
+        for h in range(Hq):
+            g = h // G
+            o, s = _row_softmax(q[t][h], [k[j][g] for j in keys], [v[j][g] for j in keys],
+                                scale, 1.0)
+            out[t][h] = o
+            lse[h][t] = s
+    return out, lse

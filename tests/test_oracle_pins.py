@@ -558,3 +558,70 @@ def test_decode_q_fixed_layout_is_packed_layout():
     op, lp = A.decode_q_reference(f64(case.q).reshape(12, 4, 8), *args, qo_indptr=qo)
     cmp(o.reshape(12, 4, 8), op)
     cmp(l.reshape(12, 4), lp)
+
+
+# ----------------------------------------------------------------------------- QSA
+
+@pytest.mark.parametrize("mode", ["causal", "dense"])
+def test_qsa_matches_bruteforce(mode):
+    case = W.make_qsa(50, [7, 10, 5], Hq=4, Hkv=2, D=16, p_sel=0.4, mode=mode, empty_rows=2,
+                      junk_bits=0.2)
+    out, lse = A.qsa_reference(case.q, case.k, case.v, case.sel_blocks, case.lo, case.hi,
+                               case.block_first, case.block_last, case.scale)
+    bo, bl = BF.qsa_bruteforce(case.q, case.k, case.v, case.sel_blocks, case.lo, case.hi,
+                               case.block_first, case.block_last, case.scale)
+    cmp(out, np.array(bo), 1e-12)
+    cmp(lse, np.array(bl), 1e-12)
+    empty = case.lo > case.hi
+    assert empty.sum() == 2
+    assert np.all(out[empty] == 0.0) and np.all(lse[:, empty] == -np.inf)
+
+
+def test_qsa_all_blocks_causal_equals_per_sequence_sdpa():
+    """Every block selected with lo = sequence start, hi = t is causal attention
+    inside each packed sequence (torch fp64 SDPA, GQA by repeat_interleave)."""
+    lens = [37, 64, 9]
+    case = W.make_qsa(51, lens, Hq=6, Hkv=2, D=32, p_sel=1.0, mode="causal")
+    out, lse = A.qsa_reference(case.q, case.k, case.v, case.sel_blocks, case.lo, case.hi,
+                               case.block_first, case.block_last, case.scale)
+    t0 = 0
+    for L in lens:
+        qs = case.q[t0:t0 + L].to(torch.float64).transpose(0, 1)
+        ks = case.k[t0:t0 + L].to(torch.float64).transpose(0, 1).repeat_interleave(3, 0)
+        vs = case.v[t0:t0 + L].to(torch.float64).transpose(0, 1).repeat_interleave(3, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, is_causal=True,
+                                                               scale=case.scale)
+        cmp(out[t0:t0 + L], ref.transpose(0, 1).numpy(), 1e-12)
+        s = (qs @ ks.transpose(1, 2)) * case.scale
+        s = s.masked_fill(torch.ones(L, L, dtype=torch.bool).triu(1), -math.inf)
+        cmp(lse[:, t0:t0 + L], torch.logsumexp(s, -1).numpy(), 1e-12)
+        t0 += L
+
+
+def test_qsa_single_key_rows_and_out_of_bound_bits():
+    """Selecting only the token's own block with lo = hi = t leaves one key: out =
+    v[t], LSE = scale*<q, k_t>.  Bits set on blocks outside [lo, hi] change
+    nothing."""
+    case = W.make_qsa(52, [13, 6], Hq=2, Hkv=1, D=16, p_sel=0.0, mode="causal")
+    lo = np.arange(19, dtype=np.int32)
+    out, lse = A.qsa_reference(case.q, case.k, case.v, case.sel_blocks, lo, lo,
+                               case.block_first, case.block_last, case.scale)
+    qf, kf, vf = (x.to(torch.float64).numpy() for x in (case.q, case.k, case.v))
+    cmp(out, np.repeat(vf, 2, axis=1), 1e-12)
+    cmp(lse, (np.einsum("thd,td->ht", qf, kf[:, 0]) * case.scale), 1e-12)
+    junk = case.sel_blocks.copy()
+    junk[:, :] = 1
+    out2, lse2 = A.qsa_reference(case.q, case.k, case.v, junk, lo, lo, case.block_first,
+                                 case.block_last, case.scale)
+    cmp(out2, out, 0.0)
+    cmp(lse2, lse, 0.0)
+
+
+def test_qsa_partition_spans():
+    """Block numbering restarts per sequence: a sequence of length L owns
+    ceil(L/4) consecutive global blocks of 4 tokens, the last one partial."""
+    from gen.workloads import qsa_partition
+    tb, bb, bf, bl = qsa_partition([7, 4, 1])
+    assert tb.tolist() == [0] * 7 + [7] * 4 + [11]
+    assert bb.tolist() == [0] * 7 + [2] * 4 + [3]
+    assert bf.tolist() == [0, 4, 7, 11] and bl.tolist() == [3, 6, 10, 11]
