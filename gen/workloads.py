@@ -582,6 +582,14 @@ def make_sage(seed, B, H, Sq, Sk, cap, nsel=None, per_row_counts=True, count_lo=
                     index, bsn, bsz, nums, uniform, None, Sk, name)
 
 
+def qsa_long(seed=7, n_seq=4, seq_len=4096, n_sel=64):
+    """Token-granular sparse attention at the page's geometry: 4 packed causal
+    sequences of 4096 tokens, Hq=12 / Hkv=1, D=256, 4-token blocks; every token
+    selects up to 64 random blocks of its causal range plus its own block."""
+    return make_qsa(seed, [seq_len] * n_seq, Hq=12, Hkv=1, D=256, mode="causal",
+                    n_sel=n_sel, name=f"qsa_{n_seq}x{seq_len}_sel{n_sel}")
+
+
 def sage_long(seed=5):
     """B=2, H=16, Sq=Sk=16384, D=128, 64-token blocks, each Q block selects 25%
     (64 of 256) KV blocks at random (non-contiguous), per-row counts supplied,

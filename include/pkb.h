@@ -13,6 +13,8 @@
  *     (page "flashinfer.attention.prims_ts.prims_ts_batch_decode_with_kv_cache")
  *                                                        -> paged_decode_validate / _workspace_size / _run
  *     multi-token (fixed SQ or packed qo_indptr) decode   -> paged_decode_q_validate / _workspace_size / _run
+ *   - packed-query token-granular sparse attention
+ *     (page "flashinfer.qsa.qsa_forward")                -> qsa_validate / qsa_run
  *   - prequantized Sage-style block-sparse attention
  *     (page "flashinfer.cute_dsl.sparse.bsa_attn_sm120.bsa_attn_sm120_blk64_sage_fwd")
  *                                                        -> bsa_sage_validate / bsa_sage_run
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PKB_ABI_VERSION 1
+#define PKB_ABI_VERSION 2
 
 /* Largest max_seq_len accepted: 2^31 - 128, so that a 128-token padded tile end
  * still fits in int32 (page "prims_ts_batch_decode_with_kv_cache", description of
@@ -89,7 +91,13 @@ enum pkb_field {
   PKB_FIELD_BLOCK_TABLES = 7,
   PKB_FIELD_Q2K_INDEX = 8,
   PKB_FIELD_Q2K_NUMS = 9,
-  PKB_FIELD_BLOCK_SIZES = 10
+  PKB_FIELD_BLOCK_SIZES = 10,
+  PKB_FIELD_LO = 11,
+  PKB_FIELD_HI = 12,
+  PKB_FIELD_BLK_BASE = 13,
+  PKB_FIELD_TOK_BASE = 14,
+  PKB_FIELD_BLOCK_FIRST = 15,
+  PKB_FIELD_BLOCK_LAST = 16
 };
 
 /* First contract violation found by a *_validate call: the array and the flat
@@ -394,6 +402,43 @@ int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
                  int32_t uniform_block_count, int32_t contiguous_block_indices,
                  int32_t B, int32_t H, int32_t Sq, int32_t Sk, float softmax_scale,
                  int32_t mask_type, void* out, float* lse, void* stream);
+
+/* ======================================================================== */
+/* Packed-query token-granular sparse attention                              */
+/* (page "qsa_forward": signature, Parameters, Returns, Notes)                */
+/* ======================================================================== */
+
+/* Host validation of the packed partition (host copies, all [T] or [NB] int32):
+ *   tok_base: a token starting a sequence has tok_base[t] == t, every other
+ *     token repeats its predecessor's value (TOK_BASE, t);
+ *   blk_base: constant inside a sequence and, with the sequence's
+ *     ceil(len/4) blocks, inside [0, NB) (BLK_BASE, t);
+ *   block_first / block_last of block blk_base + m of a sequence starting at s0
+ *     with length len: s0 + 4m and min(s0 + 4m + 3, s0 + len - 1)
+ *     (BLOCK_FIRST / BLOCK_LAST, block index);
+ *   lo / hi: when lo[t] <= hi[t], both inside t's sequence (LO / HI, t);
+ *     lo[t] > hi[t] is an empty row.
+ * Order: per token in order tok_base, blk_base; then blocks; then lo, hi.
+ * Static errors: T < 1, NB < 1 or a NULL array -> PKB_ERR_ARG. */
+int qsa_validate(int32_t T, int32_t NB, const int32_t* lo_h, const int32_t* hi_h,
+                 const int32_t* blk_base_h, const int32_t* tok_base_h,
+                 const int32_t* block_first_h, const int32_t* block_last_h, pkb_bad_t* bad);
+
+/* Trusted run.  q [T, Hq, D] bf16, k / v [T, Hkv, D] bf16 (packed tokens, not
+ * paged), sel_blocks [T, NB] uint8 (nonzero selects a global block), lo / hi /
+ * blk_base / tok_base [T] int32 on the device, satisfying qsa_validate.
+ * block_first / block_last need not be passed: under the partition contract a
+ * block's span follows from tok_base and blk_base, which the kernel uses.
+ * D in {128, 256} (the page: 256), Hq / Hkv <= 16 (the page: 12), block_size
+ * must be 4, scale finite (used as given; the page's default is 1/sqrt(256)).
+ * Outputs (each may be NULL, not all): out [T, Hq, D] bf16, out_f32
+ * [T, Hq, D], lse [Hq, T] natural log (the page's layout).  Empty rows give
+ * zeros and -inf. */
+int qsa_run(const void* q, const void* k, const void* v, const uint8_t* sel_blocks,
+            const int32_t* lo, const int32_t* hi, const int32_t* blk_base,
+            const int32_t* tok_base, int32_t T, int32_t NB, int32_t Hq, int32_t Hkv,
+            int32_t D, float scale, int32_t block_size, void* out, float* out_f32,
+            float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,6 +38,7 @@ PKB_ERR_WORKSPACE = -6
 F_NONE, F_KV_INDPTR, F_KV_INDICES, F_SEQ_LENS = 0, 1, 2, 3
 F_BLOCK_INDPTR, F_BLOCK_INDICES, F_QO_INDPTR, F_BLOCK_TABLES = 4, 5, 6, 7
 F_Q2K_INDEX, F_Q2K_NUMS, F_BLOCK_SIZES = 8, 9, 10
+F_LO, F_HI, F_BLK_BASE, F_TOK_BASE, F_BLOCK_FIRST, F_BLOCK_LAST = 11, 12, 13, 14, 15, 16
 
 BF16, FP32 = 0, 1
 DENSE, CAUSAL = 0, 1
@@ -409,4 +410,56 @@ def sage_validate(index, capacity, block_sparse_num, block_sizes, nums, uniform,
         for f, x in enumerate(np.asarray(block_sizes, dtype=np.int64).ravel()):
             if not (0 <= x <= 64):
                 return _bad(F_BLOCK_SIZES, f)
+    return OK
+
+
+# ----------------------------------------------------------------------------
+# QSA
+# ----------------------------------------------------------------------------
+
+def qsa_validate(lo, hi, blk_base, tok_base, block_first, block_last):
+    """Page "qsa_forward", Notes: the metadata must describe one consistent packed
+    partition.  Sequences are the runs of tokens sharing tok_base (starting at
+    their own index); a sequence of length L at s0 owns blocks blk_base ..
+    blk_base + ceil(L/4) - 1 inside [0, NB), block m spanning s0 + 4m ..
+    min(s0 + 4m + 3, s0 + L - 1) (block_size 4, numbering restarting per
+    sequence); lo/hi lie inside the sequence unless lo > hi (an empty row)."""
+    lo, hi, bb, tb = (np.asarray(x, np.int64) for x in (lo, hi, blk_base, tok_base))
+    bf, bl = np.asarray(block_first, np.int64), np.asarray(block_last, np.int64)
+    T, NB = lo.size, bf.size
+    if T < 1 or NB < 1:
+        return PKB_ERR_ARG, F_NONE, -1
+    seq_end = np.zeros(T, np.int64)
+    t = 0
+    while t < T:
+        if tb[t] != t:
+            return _bad(F_TOK_BASE, t)
+        e = t + 1
+        while e < T and tb[e] == t:
+            e += 1
+        if e < T and tb[e] != e:
+            return _bad(F_TOK_BASE, e)
+        nblk = cdiv(e - t, 4)
+        for u in range(t, e):
+            if bb[u] != bb[t] or bb[t] < 0 or bb[t] + nblk > NB:
+                return _bad(F_BLK_BASE, u)
+            seq_end[u] = e - 1
+        t = e
+    t = 0
+    while t < T:
+        e = int(seq_end[t]) + 1
+        for m in range(cdiv(e - t, 4)):
+            nb = int(bb[t]) + m
+            if bf[nb] != t + 4 * m:
+                return _bad(F_BLOCK_FIRST, nb)
+            if bl[nb] != min(t + 4 * m + 3, e - 1):
+                return _bad(F_BLOCK_LAST, nb)
+        t = e
+    for t in range(T):
+        if lo[t] > hi[t]:
+            continue
+        if lo[t] < tb[t] or lo[t] > seq_end[t]:
+            return _bad(F_LO, t)
+        if hi[t] > seq_end[t]:
+            return _bad(F_HI, t)
     return OK

@@ -32,6 +32,9 @@ from .ops import (  # noqa: E402
     paged_prefill_plan_capacity,
     paged_prefill_run,
     paged_prefill_validate,
+    qsa_forward,
+    qsa_run,
+    qsa_validate,
     split_kv_cache,
 )
 
@@ -42,5 +45,6 @@ __all__ = [
     "bsa_run", "bsa_sage_run", "bsa_sage_validate", "bsa_validate", "num_cus",
     "paged_decode_q_run", "paged_decode_q_validate", "paged_decode_q_workspace_size",
     "paged_decode_run", "paged_decode_validate", "paged_decode_workspace_size",
-    "paged_prefill_plan", "paged_prefill_plan_capacity", "paged_prefill_run", "paged_prefill_validate", "split_kv_cache",
+    "paged_prefill_plan", "paged_prefill_plan_capacity", "paged_prefill_run",
+    "paged_prefill_validate", "qsa_forward", "qsa_run", "qsa_validate", "split_kv_cache",
 ]

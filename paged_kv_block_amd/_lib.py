@@ -27,7 +27,8 @@ PKB_MAX_SEQ_LEN = 2147483520
 
 FIELD_NAMES = {0: "none", 1: "paged_kv_indptr", 2: "paged_kv_indices", 3: "seq_lens",
                4: "block_indptr", 5: "block_indices", 6: "qo_indptr", 7: "block_tables",
-               8: "q2k_block_index", 9: "q2k_block_nums", 10: "block_sizes"}
+               8: "q2k_block_index", 9: "q2k_block_nums", 10: "block_sizes", 11: "lo",
+               12: "hi", 13: "blk_base", 14: "tok_base", 15: "block_first", 16: "block_last"}
 
 
 class BsaStaticArgs(ctypes.Structure):
@@ -101,6 +102,11 @@ _SIGS = {
                                    c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                    c_int32, c_float, c_float, c_int32, c_void_p, c_void_p,
                                    c_void_p, c_size_t, c_int32, c_void_p]),
+    "qsa_validate": (c_int, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                             c_void_p, POINTER(Bad)]),
+    "qsa_run": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                        c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_int32,
+                        c_void_p, c_void_p, c_void_p, c_void_p]),
     "bsa_sage_validate": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p,
                                   c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(Bad)]),
     "bsa_sage_run": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -371,4 +371,37 @@ int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
   return hip_status(pkb::launch_sage(p, (hipStream_t)stream));
 }
 
+int qsa_run(const void* q, const void* k, const void* v, const uint8_t* sel_blocks,
+            const int32_t* lo, const int32_t* hi, const int32_t* blk_base,
+            const int32_t* tok_base, int32_t T, int32_t NB, int32_t Hq, int32_t Hkv,
+            int32_t D, float scale, int32_t block_size, void* out, float* out_f32, float* lse,
+            void* stream) {
+  if (T < 1 || NB < 1 || Hq < 1 || Hkv < 1) return PKB_ERR_ARG;
+  if (Hq % Hkv) return PKB_ERR_SHAPE;
+  if (block_size != 4 || (D != 128 && D != 256) || Hq / Hkv > 16) return PKB_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return PKB_ERR_ARG;
+  if (!q || !k || !v || !sel_blocks || !lo || !hi || !blk_base || !tok_base) return PKB_ERR_ARG;
+  if (!out && !out_f32 && !lse) return PKB_ERR_ARG;
+  pkb::QsaParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.sel = sel_blocks;
+  p.lo = lo;
+  p.hi = hi;
+  p.blk_base = blk_base;
+  p.tok_base = tok_base;
+  p.out = (uint16_t*)out;
+  p.out_f32 = out_f32;
+  p.lse = lse;
+  p.T = T;
+  p.NB = NB;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(pkb::launch_qsa(p, D, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -422,4 +422,46 @@ int bsa_sage_validate(const int32_t* index, int32_t capacity, int32_t block_spar
   return PKB_OK;
 }
 
+// ------------------------------------------------------------------ QSA
+
+int qsa_validate(int32_t T, int32_t NB, const int32_t* lo, const int32_t* hi,
+                            const int32_t* blk_base, const int32_t* tok_base,
+                            const int32_t* block_first, const int32_t* block_last,
+                            pkb_bad_t* bad) {
+  clear_bad(bad);
+  if (T < 1 || NB < 1 || !lo || !hi || !blk_base || !tok_base || !block_first || !block_last)
+    return PKB_ERR_ARG;
+  // sequences: runs of tokens sharing tok_base, each starting at its own index
+  std::vector<int32_t> seq_end(T);
+  for (int32_t t = 0; t < T;) {
+    if (tok_base[t] != t) return set_bad(bad, PKB_FIELD_TOK_BASE, t);
+    int32_t e = t + 1;
+    while (e < T && tok_base[e] == t) ++e;
+    if (e < T && tok_base[e] != e) return set_bad(bad, PKB_FIELD_TOK_BASE, e);
+    const int64_t nblk = cdiv(e - t, 4);
+    for (int32_t u = t; u < e; ++u) {
+      if (blk_base[u] != blk_base[t] || blk_base[t] < 0 || blk_base[t] + nblk > NB)
+        return set_bad(bad, PKB_FIELD_BLK_BASE, u);
+      seq_end[u] = e - 1;
+    }
+    t = e;
+  }
+  for (int32_t t = 0; t < T;) {
+    const int32_t e = seq_end[t] + 1;
+    for (int64_t m = 0; m < cdiv(e - t, 4); ++m) {
+      const int64_t nb = blk_base[t] + m;
+      if (block_first[nb] != t + 4 * m) return set_bad(bad, PKB_FIELD_BLOCK_FIRST, nb);
+      if (block_last[nb] != std::min<int64_t>(t + 4 * m + 3, e - 1))
+        return set_bad(bad, PKB_FIELD_BLOCK_LAST, nb);
+    }
+    t = e;
+  }
+  for (int32_t t = 0; t < T; ++t) {
+    if (lo[t] > hi[t]) continue;
+    if (lo[t] < tok_base[t] || lo[t] > seq_end[t]) return set_bad(bad, PKB_FIELD_LO, t);
+    if (hi[t] > seq_end[t]) return set_bad(bad, PKB_FIELD_HI, t);
+  }
+  return PKB_OK;
+}
+
 }  // extern "C"

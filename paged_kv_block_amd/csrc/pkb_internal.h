@@ -93,10 +93,28 @@ struct SageParams {
   float scale_log2;
 };
 
+// Packed-query token-granular sparse attention (non-paged packed K/V).
+struct QsaParams {
+  const uint16_t* q;          // [T, Hq, D]
+  const uint16_t* k;          // [T, Hkv, D]
+  const uint16_t* v;
+  const uint8_t* sel;         // [T, NB]
+  const int32_t* lo;          // [T] inclusive key bounds
+  const int32_t* hi;
+  const int32_t* blk_base;    // [T] first global block / token of the token's sequence
+  const int32_t* tok_base;
+  uint16_t* out;              // [T, Hq, D] bf16 or null
+  float* out_f32;             // [T, Hq, D] or null
+  float* lse;                 // [Hq, T] or null
+  int T, NB, Hq, Hkv, G;
+  float scale_log2;
+};
+
 hipError_t launch_attn(const AttnParams& p, int D, int waves, int mode, dim3 grid,
                        hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int D, int grid, hipStream_t stream);
 hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream);
 hipError_t launch_sage(const SageParams& p, hipStream_t stream);
+hipError_t launch_qsa(const QsaParams& p, int D, hipStream_t stream);
 
 }  // namespace pkb

@@ -543,3 +543,64 @@ def bsa_attn_blk64_sage_fwd(q_int8, k_int8, v_fp8, q_scale, k_scale, v_scale, q2
                         uniform_block_count=uniform_block_count,
                         contiguous_block_indices=contiguous_block_indices, mask_type=mask_type,
                         lse=lse)
+
+
+# =============================================================================
+# Packed-query token-granular sparse attention
+# =============================================================================
+
+def qsa_validate(lo, hi, blk_base, tok_base, block_first, block_last, raise_on_error=True):
+    """Host check of the packed partition (copies device tensors to the host)."""
+    a = [_host_i32(x) for x in (lo, hi, blk_base, tok_base, block_first, block_last)]
+    bad = Bad()
+    st = lib().qsa_validate(a[0].size, a[4].size, *[_hp(x) for x in a], ctypes.byref(bad))
+    if raise_on_error:
+        check(st, "qsa_validate", bad)
+    return st, bad.field, bad.index
+
+
+def qsa_run(q, k, v, sel_blocks, lo, hi, blk_base, tok_base, scale=0.0625, block_size=4, *,
+            out=None, out_fp32=None, lse=None, stream=None):
+    """Trusted launch; any of out (bf16), out_fp32, lse [Hq, T] may be given."""
+    T, Hq, D = q.shape
+    _need(q.dtype == torch.bfloat16 and k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16,
+          "q, k, v must be bf16")
+    _need(k.dim() == 3 and k.shape == v.shape and k.shape[0] == T and k.shape[2] == D,
+          "k, v must be [T, Hkv, D]")
+    _need(sel_blocks.dtype == torch.uint8 and sel_blocks.dim() == 2 and sel_blocks.shape[0] == T,
+          "sel_blocks must be uint8 [T, NB]")
+    for t in (q, k, v, sel_blocks):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous CUDA tensors")
+    for t, n in ((lo, "lo"), (hi, "hi"), (blk_base, "blk_base"), (tok_base, "tok_base")):
+        _dev_i32(t, n)
+        _need(t.numel() == T, f"{n} must be [T]")
+    if out is not None:
+        _need(out.dtype == torch.bfloat16 and out.shape == q.shape and out.is_contiguous(),
+              "out must be bf16 [T, Hq, D]")
+    if out_fp32 is not None:
+        _need(out_fp32.dtype == torch.float32 and out_fp32.shape == q.shape
+              and out_fp32.is_contiguous(), "out_fp32 must be fp32 [T, Hq, D]")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and tuple(lse.shape) == (Hq, T) and lse.is_contiguous(),
+              "lse must be fp32 [Hq, T]")
+    st = lib().qsa_run(_ptr(q), _ptr(k), _ptr(v), _ptr(sel_blocks), _ptr(lo), _ptr(hi),
+                       _ptr(blk_base), _ptr(tok_base), T, sel_blocks.shape[1], Hq, k.shape[1], D,
+                       float(scale), int(block_size), _ptr(out), _ptr(out_fp32), _ptr(lse),
+                       stream if stream is not None else _stream(q.device))
+    check(st, "qsa_run")
+
+
+def qsa_forward(q, k, v, sel_blocks, lo, hi, blk_base, tok_base, block_first, block_last,
+                scale=0.0625, block_size=4, validate=False):
+    """Mirrors the page "qsa_forward": returns (out bf16, out_fp32, lse [Hq, T]).
+    ``validate`` checks the packed partition on the host first (a device->host
+    copy; leave it off inside graph capture)."""
+    if validate:
+        qsa_validate(lo, hi, blk_base, tok_base, block_first, block_last)
+    T, Hq, D = q.shape
+    out = torch.empty_like(q)
+    out_fp32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(Hq, T, dtype=torch.float32, device=q.device)
+    qsa_run(q, k, v, sel_blocks, lo, hi, blk_base, tok_base, scale, block_size, out=out,
+            out_fp32=out_fp32, lse=lse)
+    return out, out_fp32, lse

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     L = P.lib()
-    assert L.pkb_abi_version() == 1
+    assert L.pkb_abi_version() == 2
     for st in range(0, -8, -1):
         assert L.pkb_status_string(st).decode() not in ("", "unknown status")
     assert M.MAX_SEQ_LEN == 2147483520 == C.PKB_MAX_SEQ_LEN   # 2^31 - 128
@@ -413,3 +413,32 @@ def test_sage_validate_matches_spec():
                                        raise_on_error=False)
         got = (st, f, i) if st == M.PKB_ERR_METADATA else (st, 0, -1)
         assert got == want, (t, got, want)
+
+
+# ----------------------------------------------------------------------------- QSA
+
+def test_qsa_validate_matches_spec():
+    rng = np.random.default_rng(6)
+    case = W.make_qsa(60, [9, 1, 14, 4, 7], Hq=2, Hkv=1, D=16, p_sel=0.3, empty_rows=2)
+    base = [case.lo, case.hi, case.blk_base, case.tok_base, case.block_first, case.block_last]
+    n_bad = 0
+    for t in range(400):
+        a = [x.copy() for x in base]
+        k = t % 7
+        if t < 3:
+            pass
+        else:
+            which = int(rng.integers(0, 6))
+            arr = a[which]
+            i = int(rng.integers(0, arr.size))
+            arr[i] += int(rng.choice([-5, -1, 1, 2, 40]))
+            if k == 6:      # a second, independent change
+                arr2 = a[int(rng.integers(0, 6))]
+                arr2[int(rng.integers(0, arr2.size))] = int(rng.integers(-2, 40))
+        want = M.qsa_validate(*a)
+        st, f, i = P.qsa_validate(*a, raise_on_error=False)
+        got = (st, f, i) if st == M.PKB_ERR_METADATA else (st, 0, -1)
+        assert got == want, (t, got, want)
+        n_bad += want[0] != 0
+    assert n_bad > 150
+    assert M.qsa_validate(*base) == M.OK
