@@ -370,6 +370,47 @@ def bench_sage(steps, warmup, W, P):
                          "traffic": measured_traffic(["sage_kernel"], "sage"), "kernel": "sage_kernel"}}
 
 
+def bench_qsa(steps, warmup, W, P):
+    log("qsa: generating inputs")
+    case = W.qsa_long()
+    T, Hq, D = case.q.shape
+    Hkv = case.k.shape[1]
+    q, k, v = case.q.cuda(), case.k.cuda(), case.v.cuda()
+    sel = torch.from_numpy(case.sel_blocks).cuda()
+    lo, hi, bb, tb = (dev_i32(x) for x in (case.lo, case.hi, case.blk_base, case.tok_base))
+    P.qsa_validate(case.lo, case.hi, case.blk_base, case.tok_base, case.block_first,
+                   case.block_last)
+    out = torch.empty_like(q)
+    out32 = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    lse = torch.empty(Hq, T, dtype=torch.float32, device="cuda")
+
+    def step():
+        P.qsa_run(q, k, v, sel, lo, hi, bb, tb, case.scale, out=out, out_fp32=out32, lse=lse)
+
+    ms_step, ms_launch = time_launches(step, steps, warmup)
+    # admitted (token, key) pairs: the selected blocks' tokens inside [lo, hi]
+    bf, bl = case.block_first.astype(np.int64), case.block_last.astype(np.int64)
+    pairs = 0
+    for t in range(T):
+        nb = np.nonzero(case.sel_blocks[t])[0]
+        a = np.maximum(bf[nb], case.lo[t])
+        b = np.minimum(bl[nb], case.hi[t])
+        pairs += int(np.maximum(b - a + 1, 0).sum())
+    flops = 4.0 * D * pairs * Hq
+    gathered = pairs * Hkv * D * 2 * 2          # K + V rows read per (token, KV head)
+    tf = flops / (ms_step * 1e-3) / 1e12
+    ach = flops / (ms_launch * 1e-3) / 1e12
+    return {"workload": f"packed token-granular sparse attention T={T} (4x4096 causal) Hq={Hq} "
+                        f"Hkv={Hkv} D={D} 4-token blocks, <=64 selected blocks per token",
+            "metric": "QSA TFLOP/s (admitted pairs)", "value": round(tf, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
+            "gathered_kv_GBps": round(gathered / (ms_launch * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic(["qsa_kernel<256>"], "qsa"),
+                         "kernel": "qsa_kernel<256>"}}
+
+
 def bench_copy():
     """A plain 1 GiB device-to-device copy, three times: the calibration run
     for the FETCH_SIZE / WRITE_SIZE counters (what they read for known bytes)."""
@@ -416,7 +457,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["decode", "decode_q", "bsa", "prefill", "prefill256", "tiny",
-                                       "sage", "copy"], default=None,
+                                       "sage", "qsa", "copy"], default=None,
                     help="run one workload only (for profiling; copy = counter calibration)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -437,6 +478,7 @@ def main(argv=None):
               "tiny": lambda: bench_bsa_tiny(a.steps, a.warmup, W, P),
               "sage": lambda: bench_sage(a.steps, a.warmup, W, P),
               "decode_q": lambda: bench_decode_q(a.steps, a.warmup, W, P),
+              "qsa": lambda: bench_qsa(a.steps, a.warmup, W, P),
               "copy": bench_copy}[a.only]
         print(json.dumps(fn()), flush=True)
         return 0
@@ -451,6 +493,7 @@ def main(argv=None):
                    lambda: bench_prefill(a.steps, a.warmup, W, P, D=256),
                    lambda: bench_sage(a.steps, a.warmup, W, P),
                    lambda: bench_decode_q(a.steps, a.warmup, W, P),
+                   lambda: bench_qsa(a.steps, a.warmup, W, P),
                    lambda: bench_bsa_tiny(a.steps, a.warmup, W, P)):
             r = fn()
             log(f"{r['workload']}: {r['value']} {r['unit']}")

@@ -18,9 +18,9 @@
 //
 // Each token's key set is its own, so keys are never shared between tokens:
 // one wave handles one (token, KV head) and gathers exactly the keys it admits.
-//   * candidate blocks go 64 at a time: each lane loads one bitmap byte and a
-//     ballot gives the window's selected blocks as a scalar mask; selected block
-//     ids are peeled off 8 at a time (a group of 32 keys) with scalar bit scans;
+//   * candidate blocks go 1024 at a time into a per-wave LDS list of the
+//     selected ones (bitmap bytes tested per lane, placed by a prefix sum);
+//     groups of 8 selected blocks (32 keys) are read from it;
 //   * per group, S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (M = 16 keys, N = the
 //     query heads of the KV head, at most 16); each lane loads its key row's 16
 //     bytes straight into the A operand, and lane group g of the accumulator
@@ -40,12 +40,14 @@ namespace pkb {
 namespace {
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 constexpr int kQsaXcds = 8;
+constexpr int kChunk = 1024;       // candidate blocks per selected-block list
 
 template <int D>
 struct QsaLayout {
   static constexpr int KEYS = 32;              // keys per group (8 blocks of 4)
   static constexpr int VROW = D * 2 + 32;      // padded V row: transpose reads hit distinct banks
-  static constexpr int LDS = KEYS * VROW;
+  static constexpr int LDS = KEYS * VROW;     // V slab; the block list follows it
+  static constexpr int LDS_TOTAL = LDS + kChunk * 2;
   static constexpr int VP = KEYS * D / 8 / 64; // 16-byte V pieces per lane per group
 };
 }  // namespace
@@ -81,41 +83,63 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
   }
   const uint8_t* selrow = p.sel + (int64_t)t * p.NB;
 
-  // ---- selected-block enumeration (scalar) ----
-  int win = nb_lo;                                   // first candidate of the loaded window
-  uint64_t mask = 0;                                 // selected, not yet taken, in window win - 64
-  int wb = 0;                                        // this lane's byte of window `win`
-  auto load_window = [&]() {
-    wb = 0;
-    if (win + lane <= nb_hi) wb = selrow[win + lane];
-  };
-  int mbase = 0;                                     // first candidate of `mask`'s window
-  auto refill = [&]() -> bool {                      // false: no candidates left
-    while (mask == 0) {
-      if (win > nb_hi) return false;
-      mask = __ballot(wb != 0);
-      mbase = win;
-      win += 64;
-      load_window();
-    }
-    return true;
-  };
-  // take the next 8 selected blocks (id -1 when exhausted); returns the count
-  auto take8 = [&](int (&id)[8]) -> int {
-    int n = 0;
+  // ---- selected-block list ----
+  // Candidates go kChunk at a time: lane l tests blocks cb + 16l .. cb + 16l + 15,
+  // a wave-wide prefix sum of the counts places the selected ones, in order,
+  // into this wave's LDS list (16-bit offsets from cb).  Groups then read 8
+  // list entries from LDS, which never waits on the K/V loads in flight.
+  uint16_t* list = (uint16_t*)(smem + Lay::LDS);
+  int cb = nb_lo;          // first candidate of the current list
+  int n_list = 0;          // entries in the current list
+  int taken = 0;           // entries already handed out
+  auto build = [&]() {
+    // 16 unconditional byte loads (index clamped into the range) all in flight
+    uint8_t x[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      id[k] = -1;
-      if (refill()) {
-        const int bit = __builtin_ctzll(mask);
-        mask &= mask - 1;
-        id[k] = mbase + bit;
-        ++n;
-      }
+    for (int b = 0; b < 16; ++b) x[b] = selrow[min(cb + 16 * lane + b, nb_hi)];
+    int flags = 0;
+#pragma unroll
+    for (int b = 0; b < 16; ++b)
+      if (cb + 16 * lane + b <= nb_hi && x[b] != 0) flags |= 1 << b;
+    const int cnt = __builtin_popcount(flags);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
     }
+    int pos = incl - cnt;
+    while (flags) {
+      const int b = __builtin_ctz(flags);
+      flags &= flags - 1;
+      list[pos++] = (uint16_t)(16 * lane + b);
+    }
+    n_list = readlane_i32(incl, 63);
+    taken = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // next 8 selected blocks (id -1 past the end); returns how many are real
+  auto take8 = [&](int (&id)[8]) -> int {
+    while (taken >= n_list) {
+      if (n_list > 0 || taken > 0) cb += kChunk;   // the current list is used up
+      if (cb > nb_hi) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) id[k] = -1;
+        return 0;
+      }
+      build();
+      if (n_list == 0) taken = 1;                   // empty chunk: move on
+    }
+    int e = -1;
+    if (lane < 8 && taken + lane < n_list) e = cb + (int)list[taken + lane];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) id[k] = readlane_i32(e, k);
+    const int n = min(8, n_list - taken);
+    taken += 8;
     return n;
   };
-  load_window();
 
   // ---- Q^T fragments (B operand of S^T) ----
   bf16x8 qf[KS];
@@ -166,18 +190,9 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
     }
   };
 
-  int id_c[8], id_n[8], id_nn[8];
-  int n_c = take8(id_c);
-  int n_n = take8(id_n);
-  bf16x8 ka[2][KS], ka_n[2][KS];
-  u32x4 vr[VP], vr_n[VP];
-  if (n_c > 0) load_group(id_c, ka, vr);
-
-  while (n_c > 0) {
-    // next group's loads fly while this one computes; the one after is enumerated
-    if (n_n > 0) load_group(id_n, ka_n, vr_n);
-    const int n_nn = n_n > 0 ? take8(id_nn) : 0;
-
+  // One group: S^T, masks, online softmax, V slab, O^T += V^T P^T.  The K/V
+  // registers are consumed here; the caller's other buffer is loading meanwhile.
+  auto compute = [&](bf16x8 (&ka)[2][KS], u32x4 (&vr)[VP], const int (&id_c)[8]) {
     f32x4 sacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -278,14 +293,23 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
     // the slab is rewritten next iteration: keep these reads before those writes
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+  };
 
-    // rotate the pipeline
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) ka[u][s] = ka_n[u][s];
-#pragma unroll
-    for (int i = 0; i < VP; ++i) vr[i] = vr_n[i];
+  // Two register buffers in ping-pong (the loop body is unrolled twice so no
+  // buffer is ever copied: a copy would wait for the loads still in flight).
+  // Per phase: enumerate the group after next (a list rebuild may wait, but
+  // only for this phase's own group, which is needed right away), start the
+  // next group's loads, compute this one.  The next group's loads are issued
+  // even past the last group (all ids -1: in-bounds rows of the token's own
+  // sequence, never used), so no phase merges paths with different numbers of
+  // loads in flight -- such a merge would make the compute wait for all of them.
+  int id_c[8], id_n[8], id_nn[8];
+  bf16x8 kA[2][KS], kB[2][KS];
+  u32x4 vA[VP], vB[VP];
+  int n_c = take8(id_c);
+  if (n_c > 0) load_group(id_c, kA, vA);
+  int n_n = n_c > 0 ? take8(id_n) : 0;
+  auto rotate_ids = [&](int n_nn) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       id_c[k] = id_n[k];
@@ -293,6 +317,21 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
     }
     n_c = n_n;
     n_n = n_nn;
+  };
+  while (n_c > 0) {
+    {
+      const int n_nn = n_n > 0 ? take8(id_nn) : 0;
+      load_group(id_n, kB, vB);
+      compute(kA, vA, id_c);
+      rotate_ids(n_nn);
+    }
+    if (n_c == 0) break;
+    {
+      const int n_nn = n_n > 0 ? take8(id_nn) : 0;
+      load_group(id_n, kA, vA);
+      compute(kB, vB, id_c);
+      rotate_ids(n_nn);
+    }
   }
 
   // ---- epilogue: lane (qn, g) holds O^T rows 16d + 4g + i of head qn ----
@@ -329,7 +368,7 @@ static hipError_t launch_qsa_d(const QsaParams& p, hipStream_t st) {
   QsaParams arg = p;
   void* args[] = {(void*)&arg};
   return hipLaunchKernel((const void*)qsa_kernel<D>, dim3((unsigned)(per * kQsaXcds)), dim3(64),
-                         args, QsaLayout<D>::LDS, st);
+                         args, QsaLayout<D>::LDS_TOTAL, st);
 }
 
 hipError_t launch_qsa(const QsaParams& p, int D, hipStream_t stream) {
