@@ -219,7 +219,7 @@ int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv
     d.scale_log2 = sl2;
     d.out_scale = bmm2_scale;
     const int64_t items = (int64_t)B * Hkv * S;
-    const int waves = (int)std::min<int64_t>(items, (int64_t)num_cus * pkb::kDecodeWavesPerCu);
+    const int waves = (int)std::min<int64_t>(items, (int64_t)num_cus * pkb::decode_waves_per_cu(D));
     hipError_t e = pkb::launch_decode(d, D, waves, s);
     if (e != hipSuccess) return hip_status(e);
   } else {

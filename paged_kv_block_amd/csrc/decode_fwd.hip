@@ -23,7 +23,8 @@
 //     of the first 16-key unit and {16+4g..16+4g+3} of the second -- the key set
 //     its S^T accumulator already holds -- so P^T feeds the MFMA directly.
 //   * Software pipeline: group j+1's loads are in flight while group j computes
-//     (two groups per wave in registers); page IDs are translated two ahead.
+//     (two register buffers in ping-pong); page IDs are loaded two groups
+//     ahead and translated one ahead.
 // Each item writes a partial (O, m, l); a small second kernel merges the chunks
 // of every (request, head).  A kernel boundary, not an in-kernel agent-scope
 // fence, makes the partials visible: on this part such a fence writes back and
@@ -125,23 +126,29 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
     for (int d = 0; d < DB; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // element offset of the 8-token chunk (lanes 0..3: four chunks of a group)
-    auto chunk_off = [&](int grp) -> int64_t {
-      int64_t off = 0;
+    // Page translation of a group's four 8-token chunks (lanes 0..3).  The page
+    // ID load is issued two groups ahead and only used one group ahead: loads
+    // retire in issue order, so waiting for it must not also wait for the K/V
+    // loads issued after it.  Every lane loads (the index is clamped into the
+    // request's live range), so no path skips a load.
+    auto page_id = [&](int grp) -> int {
+      const int t = min(t_base + grp * 32 + 8 * (lane & 3), L - 1);
+      return ids[t / p.page_size];
+    };
+    // element offset of the chunk from its page ID; dead chunks get offset 0
+    // (page 0, always in bounds) and their keys are masked
+    auto chunk_off = [&](int grp, int id) -> int64_t {
       const int t = t_base + grp * 32 + 8 * (lane & 3);
-      if (lane < 4 && grp < n_groups && t < L) {
-        const int pi = t / p.page_size;
-        off = (int64_t)ids[pi] * p.kv_page_stride + head_off + (int64_t)(t - pi * p.page_size) * D;
-      }
-      return off;
+      if (!(lane < 4 && grp < n_groups && t < L)) return 0;
+      const int pi = t / p.page_size;
+      return (int64_t)id * p.kv_page_stride + head_off + (int64_t)(t - pi * p.page_size) * D;
     };
 
     const char* kbase = (const char*)p.k;
     const char* vbase = (const char*)p.v;
     // Loads of one 32-key group.  K goes straight into the A operand of S^T;
     // V pieces are row-major (piece lane + 64i is key 4i + lane/16 at D = 128,
-    // 2i + lane/32 at D = 256, so each load's chunk is wave-uniform).  Dead
-    // chunks have offset 0 (page 0, always in bounds); their keys are masked.
+    // 2i + lane/32 at D = 256, so each load's chunk is wave-uniform).
     auto load_group = [&](int64_t off_v, bf16x8 (&ka)[2][KS], u32x4 (&vr)[VP]) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -160,21 +167,10 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
       }
     };
 
-    // Software pipeline: group j+1 is in flight while group j computes; page
-    // translation runs two groups ahead.
-    bf16x8 ka[2][KS], ka_n[2][KS];
-    u32x4 vr[VP], vr_n[VP];
-    load_group(chunk_off(0), ka, vr);
-    int64_t nxt = chunk_off(1);
-    for (int grp = 0; grp < n_groups; ++grp) {
+    // One group: S^T, masks, online softmax, V slab, O^T += V^T P^T.
+    auto compute = [&](int grp, bf16x8 (&ka)[2][KS], u32x4 (&vr)[VP]) {
       const int t0 = t_base + grp * 32;
       const bool full = t0 >= k_lo && t0 + 32 <= k_hi;
-      // page IDs first: vmcnt retires in issue order, so the wait for this load
-      // (next iteration) must not also wait for the group loads issued after it
-      const int64_t nn = chunk_off(grp + 2);
-      if (grp + 1 < n_groups) load_group(nxt, ka_n, vr_n);
-      nxt = nn;
-
       f32x4 sacc[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -276,12 +272,35 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
       // the slab is rewritten next iteration: keep these reads before those writes
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) ka[u][s] = ka_n[u][s];
-#pragma unroll
-      for (int i = 0; i < VP; ++i) vr[i] = vr_n[i];
+    };
+
+    // Software pipeline over two register buffers, the loop unrolled twice so
+    // that no buffer is copied (a copy would wait for the loads in flight).
+    // Phase of group j: issue group j+2's page-ID load, translate group j+1's
+    // (loaded a phase earlier), issue group j+1's K/V loads, compute group j.
+    // Loads past the last group read page 0 and are never used, so every phase
+    // has the same loads in flight.
+    bf16x8 kA[2][KS], kB[2][KS];
+    u32x4 vA[VP], vB[VP];
+    {
+      const int id0 = page_id(0);
+      load_group(chunk_off(0, id0), kA, vA);
+    }
+    int id_n = page_id(1);
+    for (int grp = 0; grp < n_groups; grp += 2) {
+      {
+        const int id_nn = page_id(grp + 2);
+        load_group(chunk_off(grp + 1, id_n), kB, vB);
+        compute(grp, kA, vA);
+        id_n = id_nn;
+      }
+      if (grp + 1 >= n_groups) break;
+      {
+        const int id_nn = page_id(grp + 3);
+        load_group(chunk_off(grp + 2, id_n), kA, vA);
+        compute(grp + 1, kB, vB);
+        id_n = id_nn;
+      }
     }
 
     // ---- item result: lane (qn, g) holds O^T rows 16d + 4g + i of head qn ----
@@ -320,8 +339,6 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
   }
 }
 
-// Merge of the chunk partials, one workgroup per (request, query head): LSE-
-// weighted sum over chunks c < ceil(seq_len / CH), in chunk order.
 // Merge of one (request, query token, query head): LSE-weighted sum of its live
 // splits' partials.  Lane s holds split s's (m, l) (64 splits per pass), so the max and
 // the weights take one load round trip; the O accumulation then issues the

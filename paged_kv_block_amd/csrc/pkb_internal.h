@@ -41,9 +41,10 @@ struct AttnParams {
 };
 
 // Dedicated single-token decode kernel (GQA group of at most 16 heads): a
-// persistent grid of single-wave workgroups, kDecodeWavesPerCu per CU (one per
-// SIMD measured best: each wave keeps two 32-key groups of loads in flight).
-constexpr int kDecodeWavesPerCu = 4;
+// persistent grid of single-wave workgroups, decode_waves_per_cu(D) per CU --
+// as many as fit at once (D = 128: two per SIMD, D = 256: one), each keeping
+// one 32-key group of loads in flight while it computes the previous one.
+constexpr int decode_waves_per_cu(int D) { return D == 128 ? 8 : 4; }
 constexpr int kDecodeMaxGroup = 16;
 
 struct DecodeParams {
