@@ -225,9 +225,10 @@ def bench_decode_q(steps, warmup, W, P, SQ=4):
             "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "achieved": round(kv_bytes / (ms_launch * 1e-3) / 1e9, 1),
                          "frac": round(kv_bytes / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(["attn_fwd_kernel<128,4,decode>",
+                         "traffic": measured_traffic(["decode_kernel<128>",
                                                       "decode_merge_kernel<128>"], "decode_q"),
-                         "kernel": "attn_fwd_kernel<128,4,decode> + decode_merge_kernel<128>"}}
+                         "kernel": "decode_kernel<128> + decode_merge_kernel<128> (16 query "
+                                   "rows per KV head: 4 tokens x 4 heads)"}}
 
 
 def bench_bsa_long(steps, warmup, W, P):

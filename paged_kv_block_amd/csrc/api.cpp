@@ -215,6 +215,8 @@ int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv
     d.window_left = window_left;
     d.num_splits = S;
     d.split_len = split_len;
+    d.Sq = 1;
+    d.maxq = 1;
     d.out_f32 = out_dtype == PKB_FP32;
     d.scale_log2 = sl2;
     d.out_scale = bmm2_scale;
@@ -283,11 +285,50 @@ int paged_decode_q_run(const void* query, const void* k, const void* v, int64_t 
     return PKB_ERR_SHAPE;
   if (!isfinite(bmm2_scale)) return PKB_ERR_ARG;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKB_ERR_WORKSPACE;
-  // row tiles of the general kernel in decode mode (4 waves x 32 packed rows)
-  const int64_t rtiles = cdiv((int64_t)maxq * (Hq / Hkv), 128);
-  if (rtiles * S > 0x7fffffff) return PKB_ERR_UNSUPPORTED;
   float* part = S > 1 ? (float*)workspace : nullptr;
   const hipStream_t s = (hipStream_t)stream;
+  const float sl2 = scale_or_default(bmm1_scale, D) * 1.4426950408889634f;
+  if ((int64_t)maxq * (Hq / Hkv) <= pkb::kDecodeMaxGroup) {
+    // the query rows of a KV head fit the 16 MFMA columns of the decode kernel
+    pkb::DecodeParams d;
+    memset(&d, 0, sizeof(d));
+    d.q = (const uint16_t*)query;
+    d.k = (const uint16_t*)k;
+    d.v = (const uint16_t*)v;
+    d.out = out;
+    d.lse = lse;
+    d.part = part;
+    d.kv_indptr = kv_indptr;
+    d.kv_indices = kv_indices;
+    d.seq_lens = seq_lens;
+    d.qo_indptr = qo_indptr;
+    d.kv_page_stride = kv_page_stride;
+    d.kv_head_stride = kv_head_stride;
+    d.B = B;
+    d.Hq = Hq;
+    d.Hkv = Hkv;
+    d.G = Hq / Hkv;
+    d.page_size = page_size;
+    d.window_left = window_left;
+    d.Sq = seq_len_q;
+    d.maxq = maxq;
+    d.causal = mask_type == PKB_MASK_CAUSAL;
+    d.num_splits = S;
+    d.split_len = split_len;
+    d.out_f32 = out_dtype == PKB_FP32;
+    d.scale_log2 = sl2;
+    d.out_scale = bmm2_scale;
+    const int64_t items = (int64_t)B * Hkv * S;
+    const int waves = (int)std::min<int64_t>(items, (int64_t)num_cus * pkb::decode_waves_per_cu(D));
+    hipError_t e = pkb::launch_decode(d, D, waves, s);
+    if (e != hipSuccess) return hip_status(e);
+    if (S > 1) return launch_merge(part, seq_lens, qo_indptr, out, lse, B, maxq, seq_len_q, Hq, S,
+                                   split_len, out_dtype, bmm2_scale, D, s);
+    return PKB_OK;
+  }
+  // larger row sets: the general kernel in decode mode (4 waves x 32 packed rows)
+  const int64_t rtiles = cdiv((int64_t)maxq * (Hq / Hkv), 128);
+  if (rtiles * S > 0x7fffffff) return PKB_ERR_UNSUPPORTED;
   AttnParams p;
   memset(&p, 0, sizeof(p));
   p.q = (const uint16_t*)query;
@@ -314,7 +355,7 @@ int paged_decode_q_run(const void* query, const void* k, const void* v, int64_t 
   p.split_len = split_len;
   p.maxq = maxq;
   p.out_f32 = out_dtype == PKB_FP32;
-  p.scale_log2 = scale_or_default(bmm1_scale, D) * 1.4426950408889634f;
+  p.scale_log2 = sl2;
   p.out_scale = bmm2_scale;
   dim3 grid((unsigned)(rtiles * S), Hkv, B);
   hipError_t e = pkb::launch_attn(p, D, 4, pkb::kModeDecode, grid, s);

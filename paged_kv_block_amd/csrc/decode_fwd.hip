@@ -3,7 +3,9 @@
 // What is computed (FlashInfer page "prims_ts_batch_decode_with_kv_cache"): for
 // request b and query head h, out = bmm2_scale * softmax(bmm1_scale * q.K^T) V
 // over keys j < seq_len[b] (and j >= seq_len-1-w with a left window w >= 0),
-// plus the natural-log LSE.
+// plus the natural-log LSE.  The same kernel serves multi-token decode when
+// the query rows of one KV head (tokens x group heads) fit 16 MFMA columns:
+// token i of qlen sits at position seq_len - qlen + i (causal: keys up to it).
 //
 // The path is bound by HBM bandwidth -- every live K/V byte is read once -- so
 // the design is about keeping bytes in flight on every CU until the end:
@@ -103,9 +105,23 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
     const int c = local - (readlane_i32(incl, ln) - readlane_i32(n_b, ln));
 
     const int L = p.seq_lens[b];
-    int k_lo = p.window_left >= 0 ? max(0, L - 1 - p.window_left) : 0;
+    // MFMA column qn is query row (token i, head h) of the request: qlen tokens
+    // (one for single-token decode) x G heads, at most 16 columns.  Token i sits
+    // at position L - qlen + i and, causal, sees keys [lo_i, p_i]; otherwise
+    // [lo_i, L).  The item covers the union of those ranges inside its chunk.
+    const int qlen = p.qo_indptr ? p.qo_indptr[b + 1] - p.qo_indptr[b] : p.Sq;
+    const int tok0 = p.qo_indptr ? p.qo_indptr[b] : b * p.Sq;
+    const int qi = qn / G, qh = qn - qi * G;
+    const bool col_ok = qi < qlen;
+    const int p_col = L - qlen + qi;
+    const int hi_col = p.causal ? p_col + 1 : L;
+    const int lo_col = p.window_left >= 0 ? max(0, p_col - p.window_left) : 0;
+    int k_lo = p.window_left >= 0 ? max(0, L - qlen - p.window_left) : 0;
     k_lo = max(k_lo, c * CH);
     const int k_hi = min(L, (c + 1) * CH);
+    // keys every column admits (no per-column mask needed inside)
+    const int k_lo_all = max(p.window_left >= 0 ? max(0, L - 1 - p.window_left) : 0, c * CH);
+    const int k_hi_all = min(p.causal ? L - qlen + 1 : L, (c + 1) * CH);
     const int t_base = k_lo & ~31;
     const int n_groups = k_hi > k_lo ? (k_hi - t_base + 31) >> 5 : 0;
     const int64_t head_off = (int64_t)kvh * p.kv_head_stride;
@@ -113,11 +129,11 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
 
     bf16x8 qf[KS];
     {
-      const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + kvh * G + qn) * D + 8 * g;
+      const uint16_t* qrow = p.q + ((int64_t)(tok0 + qi) * p.Hq + kvh * G + qh) * D + 8 * g;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (qn < G) x = ld_global_16(qrow + 32 * s);
+        if (col_ok) x = ld_global_16(qrow + 32 * s);
         qf[s] = as_bf16x8(x);
       }
     }
@@ -170,7 +186,7 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
     // One group: S^T, masks, online softmax, V slab, O^T += V^T P^T.
     auto compute = [&](int grp, bf16x8 (&ka)[2][KS], u32x4 (&vr)[VP]) {
       const int t0 = t_base + grp * 32;
-      const bool full = t0 >= k_lo && t0 + 32 <= k_hi;
+      const bool full = t0 >= k_lo_all && t0 + 32 <= k_hi_all;
       f32x4 sacc[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -187,7 +203,7 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
           float sv = sacc[u][i] * p.scale_log2;
           if (!full) {
             const int t = t0 + 16 * u + 4 * g + i;
-            sv = (t >= k_lo && t < k_hi) ? sv : -INFINITY;
+            sv = (t >= k_lo && t < k_hi && t >= lo_col && t < hi_col) ? sv : -INFINITY;
           }
           sacc[u][i] = sv;
           mx = fmaxf(mx, sv);
@@ -305,10 +321,10 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
 
     // ---- item result: lane (qn, g) holds O^T rows 16d + 4g + i of head qn ----
     const float l_tot = quad_sum(l_run);
-    if (qn < G) {
-      const int hq = kvh * G + qn;
+    if (col_ok) {
+      const int hq = kvh * G + qh;
       if (S > 1) {
-        float* dst = p.part + (((int64_t)b * p.Hq + hq) * S + c) * (D + 4);
+        float* dst = p.part + ((((int64_t)b * p.maxq + qi) * p.Hq + hq) * S + c) * (D + 4);
 #pragma unroll
         for (int d = 0; d < DB; ++d) *(f32x4*)(dst + 16 * d + 4 * g) = oacc[d];
         if (g == 0) {
@@ -318,7 +334,7 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
       } else {
         const bool empty = !(l_tot > 0.f);
         const float inv = empty ? 0.f : p.out_scale / l_tot;
-        const int64_t orow = (int64_t)b * p.Hq + hq;
+        const int64_t orow = (int64_t)(tok0 + qi) * p.Hq + hq;
         if (p.out_f32) {
           float* o = (float*)p.out + orow * D;
 #pragma unroll

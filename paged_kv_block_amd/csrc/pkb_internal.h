@@ -48,17 +48,19 @@ constexpr int decode_waves_per_cu(int D) { return D == 128 ? 8 : 4; }
 constexpr int kDecodeMaxGroup = 16;
 
 struct DecodeParams {
-  const uint16_t* q;          // [B, Hq, D]
+  const uint16_t* q;          // [tokens, Hq, D]
   const uint16_t* k;
   const uint16_t* v;
-  void* out;                  // [B, Hq, D]
-  float* lse;                 // [B, Hq] or null
-  float* part;                // [B, Hq, S, D+4] or null (O, m, l, pad)
+  void* out;                  // [tokens, Hq, D]
+  float* lse;                 // [tokens, Hq] or null
+  float* part;                // [B, maxq, Hq, S, D+4] or null (O, m, l, pad)
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
   const int32_t* seq_lens;
+  const int32_t* qo_indptr;   // multi-token packed rows, or null: Sq rows per request
   int64_t kv_page_stride, kv_head_stride;
   int B, Hq, Hkv, G, page_size, window_left;
+  int Sq, maxq, causal;       // query tokens per request (fixed), partial rows, mask
   int num_splits, split_len, out_f32;
   float scale_log2;
   float out_scale;

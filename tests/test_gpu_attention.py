@@ -228,6 +228,12 @@ DECODE_Q_SWEEP = [
     (2, 32, 2, 128, [300, 5000], 32, [8, 3], "causal", -1, 64),   # 2 row tiles
     (2, 64, 1, 128, [200, 77], 16, [3, 1], "dense", -1, 256),     # G=64
     (3, 16, 4, 256, [5, 129, 700], 8, [5, 1, 4], "causal", 0, 16),  # qlen == L
+    # rows of a KV head fit 16 columns (tokens x group <= 16): the dedicated kernel
+    (4, 32, 8, 128, [9, 3000, 4, 700], 16, [1, 4, 2, 3], "causal", 40, 256),
+    (3, 16, 8, 128, [16, 2049, 90], 16, [8, 3, 1], "causal", -1, 64),
+    (2, 4, 4, 128, [16, 1500], 16, [16, 9], "causal", 5, 256),        # MHA, qlen == L
+    (2, 32, 8, 256, [333, 4097], 32, 2, "dense", -1, 256),
+    (3, 8, 2, 128, [40, 64, 50], 16, 4, "causal", -1, 256),            # one split
 ]
 
 

@@ -199,10 +199,12 @@ def test_graph_decode_replays(Hq, Hkv):
         assert_close(f64(gl), ref_l, TOL_LSE, f"lse replay {r}")
 
 
-def test_graph_decode_q_packed_replays():
-    B, Hq, Hkv, D, ps, maxlen, max_q, total_cap = 3, 32, 8, 128, 16, 2000, 6, 18
+@pytest.mark.parametrize("max_q", [6, 4])     # 6 x 4 heads: general kernel; 4 x 4: decode kernel
+def test_graph_decode_q_packed_replays(max_q):
+    B, Hq, Hkv, D, ps, maxlen, total_cap = 3, 32, 8, 128, 16, 2000, 18
     shapes = [([6, 1, 3], [6, 2000, 40]), ([1, 1, 1], [1, 1, 1]), ([5, 6, 6], [1999, 64, 700]),
               ([2, 4, 1], [100, 1000, 2000])]
+    shapes = [([min(q, max_q) for q in ql], L) for ql, L in shapes]
     cases = [W.make_decode_q(970 + r, B, Hq, Hkv, D, L, ps, qlens=ql, mask="causal",
                              extra_pages=r) for r, (ql, L) in enumerate(shapes)]
     for c in cases:
