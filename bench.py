@@ -260,7 +260,7 @@ def bench_bsa_long(steps, warmup, W, P):
             "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(["attn_fwd_kernel<128,8,bsa>"], "bsa"),
+                         "traffic": measured_traffic(["attn_fwd_kernel<128,%d,bsa>" % wr.plan.waves], "bsa"),
                          "kernel": "attn_fwd_kernel<128,%d,bsa>" % wr.plan.waves}}
 
 

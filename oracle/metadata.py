@@ -114,7 +114,7 @@ def bsa_plan(B, Sq, Hq, Hkv, D, num_pages, page_size, q_block_size, kv_block_siz
     if window_left >= 0 and mask_type != CAUSAL:
         return PKB_ERR_ARG, None
     rows = q_block_size * G
-    waves = 1 if rows <= 32 else (2 if rows <= 64 else (4 if rows <= 128 or D == 256 else 8))
+    waves = 1 if rows <= 32 else (2 if rows <= 64 else 4)
     tile_m = 32 * waves
     nqb = cdiv(Sq, q_block_size)
     tpb = cdiv(rows, tile_m)
@@ -219,7 +219,7 @@ def prefill_validate(args, qo_indptr, seq_lens, block_tables, row_stride):
 
 
 def prefill_waves(args):
-    return 8 if args["D"] == 128 else 4
+    return 4
 
 
 def prefill_tile_span(row0, tile_m, G, qlen, L, causal, window_left):

@@ -122,7 +122,7 @@ int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
   if (!plan) return PKB_ERR_ARG;
   const prefill_static_args& a = plan->a;
   if (a.B < 1 || a.Hkv < 1 || a.Hq % a.Hkv || (a.D != 128 && a.D != 256) ||
-      plan->waves != (a.D == 128 ? 8 : 4) || plan->group != a.Hq / a.Hkv)
+      plan->waves != 4 || plan->group != a.Hq / a.Hkv)
     return PKB_ERR_ARG;
   if (a.mask_type != PKB_MASK_DENSE && a.mask_type != PKB_MASK_CAUSAL) return PKB_ERR_ARG;
   if (a.window_left < -1 || (a.window_left >= 0 && a.mask_type != PKB_MASK_CAUSAL))

@@ -12,8 +12,10 @@
 // Work decomposition.  One workgroup = (request, KV head, tile of packed query
 // rows).  Query heads of one GQA group are packed into the row dimension
 // (row = token * group + head_in_group), so a KV tile loaded once serves every
-// head of the group.  Each wavefront owns 32 packed rows; up to 8 waves (two
-// per SIMD) share one KV tile.
+// head of the group.  Each wavefront owns 32 packed rows; up to 4 waves share
+// one KV tile, and two such workgroups run per CU (two waves per SIMD from
+// independent workgroups: no barrier keeps them in step, which measured faster
+// than one 8-wave workgroup).
 //
 // KV tiles are 64 keys = 8 chunks of 8 logical tokens.  An 8-token run never
 // crosses a page (page and block sizes are multiples of 8), so each chunk is one
@@ -65,6 +67,7 @@ struct AttnLayout {
   static constexpr int TILE_B = KT * ROWB;       // bytes of a K (or V) tile
   // Tiles of copy lookahead: tile t is copied LA iterations before it is read,
   // into ring slots (LA+1 per ring) whose previous tile every wave has finished.
+  // One tile ahead keeps two workgroups per CU at D = 128 (64 KB each).
   static constexpr int LA = (D == 128 && NW == 8) ? 2 : 1;
   static constexpr int NSK = LA + 1;
   static constexpr int NSV = LA + 1;
@@ -701,10 +704,8 @@ static hipError_t launch_d(const AttnParams& p, int waves, int mode, dim3 grid, 
     if (waves == 1) return launch_one<D, 1, kModeBsa>(p, grid, st);
     if (waves == 2) return launch_one<D, 2, kModeBsa>(p, grid, st);
     if (waves == 4) return launch_one<D, 4, kModeBsa>(p, grid, st);
-    if (D == 128 && waves == 8) return launch_one<128, 8, kModeBsa>(p, grid, st);
   } else if (mode == kModePrefill) {
-    if (D == 256 && waves == 4) return launch_one<256, 4, kModePrefill>(p, grid, st);
-    if (D == 128 && waves == 8) return launch_one<128, 8, kModePrefill>(p, grid, st);
+    if (waves == 4) return launch_one<D, 4, kModePrefill>(p, grid, st);
   } else if (mode == kModeDecode) {
     if (waves == 4) return launch_one<D, 4, kModeDecode>(p, grid, st);
   }

@@ -118,7 +118,9 @@ int bsa_plan(const bsa_static_args* a, bsa_plan_t* plan) {
   plan->num_q_blocks = (int)cdiv(a->Sq, a->q_block_size);
   plan->num_kv_blocks = (int)cdiv(a->max_seq_len_kv, kvbs);
   plan->valid_words = (int)cdiv(a->max_seq_len_kv, 32);
-  plan->waves = rows <= 32 ? 1 : (rows <= 64 ? 2 : (rows <= 128 || a->D == 256 ? 4 : 8));
+  // 1-4 waves of 32 rows; wider rows take several workgroups (two 4-wave
+  // workgroups per CU outran one 8-wave workgroup sharing a barrier)
+  plan->waves = rows <= 32 ? 1 : (rows <= 64 ? 2 : 4);
   plan->tile_m = 32 * plan->waves;
   plan->tiles_per_brow = (int)cdiv(rows, plan->tile_m);
   const int64_t gx = (int64_t)plan->num_q_blocks * plan->tiles_per_brow;
@@ -220,7 +222,7 @@ int paged_prefill_plan(const prefill_static_args* a, const int32_t* qo_indptr,
   if (st) return st;
   if (!qo_indptr || !seq_lens || !plan) return PKB_ERR_ARG;
   const int G = a->Hq / a->Hkv;
-  const int waves = a->D == 128 ? 8 : 4;
+  const int waves = 4;
   const int tile_m = 32 * waves;
   const bool causal = a->mask_type == PKB_MASK_CAUSAL;
   struct Item {
@@ -277,7 +279,7 @@ int paged_prefill_plan_capacity(const prefill_static_args* a, int32_t max_qlen,
   if (st) return st;
   if (!plan || max_qlen < 1 || max_qlen > a->total_q) return PKB_ERR_ARG;
   const int G = a->Hq / a->Hkv;
-  const int waves = a->D == 128 ? 8 : 4;
+  const int waves = 4;
   const int tile_m = 32 * waves;
   // every request may own up to max_qlen rows: ceil(max_qlen * G / tile_m) tiles
   // each, latest tiles first (under bottom-right causal alignment they admit
