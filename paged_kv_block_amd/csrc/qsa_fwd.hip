@@ -20,7 +20,8 @@
 // one wave handles one (token, KV head) and gathers exactly the keys it admits.
 //   * candidate blocks go 1024 at a time into a per-wave LDS list of the
 //     selected ones (bitmap bytes tested per lane, placed by a prefix sum);
-//     groups of 8 selected blocks (32 keys) are read from it;
+//     groups of 4U selected blocks (16U keys: U = 2 at D = 128, 1 at D = 256)
+//     are read from it;
 //   * per group, S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (M = 16 keys, N = the
 //     query heads of the KV head, at most 16); each lane loads its key row's 16
 //     bytes straight into the A operand, and lane group g of the accumulator
@@ -42,9 +43,12 @@ typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 constexpr int kQsaXcds = 8;
 constexpr int kChunk = 1024;       // candidate blocks per selected-block list
 
-template <int D>
+// U 16-key units (4 blocks each) per group: two at D = 128; one at D = 256,
+// which halves the K/V registers so that two waves fit per SIMD.
+template <int D, int U>
 struct QsaLayout {
-  static constexpr int KEYS = 32;              // keys per group (8 blocks of 4)
+  static constexpr int KEYS = 16 * U;          // keys per group
+  static constexpr int NB = 4 * U;             // selected blocks per group
   static constexpr int VROW = D * 2 + 32;      // padded V row: transpose reads hit distinct banks
   static constexpr int LDS = KEYS * VROW;     // V slab; the block list follows it
   static constexpr int LDS_TOTAL = LDS + kChunk * 2;
@@ -52,9 +56,11 @@ struct QsaLayout {
 };
 }  // namespace
 
-template <int D>
-__global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
-  using Lay = QsaLayout<D>;
+template <int D, int U>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+qsa_kernel(const QsaParams p) {
+  using Lay = QsaLayout<D, U>;
+  constexpr int NB = Lay::NB;
   constexpr int KS = D / 32;       // k-steps of S^T over the head dim
   constexpr int DB = D / 16;       // 16-dim blocks of O^T
   constexpr int VP = Lay::VP;
@@ -120,24 +126,24 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  // next 8 selected blocks (id -1 past the end); returns how many are real
-  auto take8 = [&](int (&id)[8]) -> int {
+  // next NB selected blocks (id -1 past the end); returns how many are real
+  auto take = [&](int (&id)[NB]) -> int {
     while (taken >= n_list) {
       if (n_list > 0 || taken > 0) cb += kChunk;   // the current list is used up
       if (cb > nb_hi) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) id[k] = -1;
+        for (int k = 0; k < NB; ++k) id[k] = -1;
         return 0;
       }
       build();
       if (n_list == 0) taken = 1;                   // empty chunk: move on
     }
     int e = -1;
-    if (lane < 8 && taken + lane < n_list) e = cb + (int)list[taken + lane];
+    if (lane < NB && taken + lane < n_list) e = cb + (int)list[taken + lane];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) id[k] = readlane_i32(e, k);
-    const int n = min(8, n_list - taken);
-    taken += 8;
+    for (int k = 0; k < NB; ++k) id[k] = readlane_i32(e, k);
+    const int n = min(NB, n_list - taken);
+    taken += NB;
     return n;
   };
 
@@ -172,9 +178,9 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
 
   // Loads of one group: K rows straight into the A operand (lane key qn of unit u
   // is token first(id[4u + qn/4]) + qn%4); V pieces row-major, one block per load.
-  auto load_group = [&](const int (&id)[8], bf16x8 (&ka)[2][KS], u32x4 (&vr)[VP]) {
+  auto load_group = [&](const int (&id)[NB], bf16x8 (&ka)[U][KS], u32x4 (&vr)[VP]) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int q4 = qn >> 2;
       const int f0 = first_tok(id[4 * u]), f1 = first_tok(id[4 * u + 1]);
       const int f2 = first_tok(id[4 * u + 2]), f3 = first_tok(id[4 * u + 3]);
@@ -192,10 +198,10 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
 
   // One group: S^T, masks, online softmax, V slab, O^T += V^T P^T.  The K/V
   // registers are consumed here; the caller's other buffer is loading meanwhile.
-  auto compute = [&](bf16x8 (&ka)[2][KS], u32x4 (&vr)[VP], const int (&id_c)[8]) {
-    f32x4 sacc[2];
+  auto compute = [&](bf16x8 (&ka)[U][KS], u32x4 (&vr)[VP], const int (&id_c)[NB]) {
+    f32x4 sacc[U];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < U; ++u) {
       sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
@@ -204,7 +210,7 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
     // lane group g of unit u holds the 4 tokens of block id_c[4u + g]
     float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int i0 = id_c[4 * u], i1 = id_c[4 * u + 1], i2 = id_c[4 * u + 2], i3 = id_c[4 * u + 3];
       const int id = g == 0 ? i0 : (g == 1 ? i1 : (g == 2 ? i2 : i3));
       const int f = first_tok(id);
@@ -229,7 +235,7 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     float ps = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e = fast_exp2(sacc[u][i] - m_use);
@@ -257,38 +263,48 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    u32x4 pw;
-    pw[0] = pack_bf16x2(sacc[0][0], sacc[0][1]);
-    pw[1] = pack_bf16x2(sacc[0][2], sacc[0][3]);
-    pw[2] = pack_bf16x2(sacc[1][0], sacc[1][1]);
-    pw[3] = pack_bf16x2(sacc[1][2], sacc[1][3]);
-    u32x4 plo = {0u, 0u, 0u, 0u};
-    if (p.out_f32) {
-      // fp32 output: P - bf16(P) enters as a second operand (~16-bit P)
+    // P^T as bf16 (B operand; lane group g holds keys 4g..4g+3 of each unit),
+    // and for fp32 output the rounding residual as a second operand (~16-bit P)
+    uint32_t pw[2 * U], plo[2 * U];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const f32x4& sa = sacc[w >> 1];
-        const int i0 = 2 * (w & 1);
+    for (int w = 0; w < 2 * U; ++w) {
+      const f32x4& sa = sacc[w >> 1];
+      const int i0 = 2 * (w & 1);
+      pw[w] = pack_bf16x2(sa[i0], sa[i0 + 1]);
+      plo[w] = 0u;
+      if (p.out_f32)
         plo[w] = pack_bf16x2(sa[i0] - __uint_as_float(pw[w] << 16),
                              sa[i0 + 1] - __uint_as_float(pw[w] & 0xFFFF0000u));
-      }
     }
+    // transpose-read addresses: lane (4r + c) of a 16-lane group reads row
+    // 4g + r of each unit, dims 16d + 4c .. +3
     const int rr = (lane & 15) >> 2, cc = lane & 3;
     const unsigned char* a0 = vs + (4 * g + rr) * Lay::VROW + 8 * cc;
-    const unsigned char* a1 = vs + (16 + 4 * g + rr) * Lay::VROW + 8 * cc;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
       const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(a0 + 32 * d));
-      const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(a1 + 32 * d));
-      const u32x2 w0 = __builtin_bit_cast(u32x2, x0);
-      const u32x2 w1 = __builtin_bit_cast(u32x2, x1);
-      u32x4 aw;
-      aw[0] = w0[0]; aw[1] = w0[1]; aw[2] = w1[0]; aw[3] = w1[1];
-      oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), as_bf16x8(pw), oacc[d], 0, 0, 0);
-      if (p.out_f32)
-        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), as_bf16x8(plo), oacc[d], 0, 0, 0);
+      if constexpr (U == 2) {
+        const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(a0 + 16 * Lay::VROW + 32 * d));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, x0);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, x1);
+        const u32x4 aw = {w0[0], w0[1], w1[0], w1[1]};
+        const u32x4 bw = {pw[0], pw[1], pw[2], pw[3]};
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), as_bf16x8(bw), oacc[d], 0, 0, 0);
+        if (p.out_f32) {
+          const u32x4 bl = {plo[0], plo[1], plo[2], plo[3]};
+          oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), as_bf16x8(bl), oacc[d], 0, 0, 0);
+        }
+      } else {
+        // one unit: K = 16 keys, v_mfma_f32_16x16x16_bf16 with the same lane layout
+        const u32x2 bw = {pw[0], pw[1]};
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(x0, __builtin_bit_cast(i16x4, bw), oacc[d], 0, 0, 0);
+        if (p.out_f32) {
+          const u32x2 bl = {plo[0], plo[1]};
+          oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(x0, __builtin_bit_cast(i16x4, bl), oacc[d], 0, 0, 0);
+        }
+      }
     }
     // the slab is rewritten next iteration: keep these reads before those writes
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -303,15 +319,15 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
   // even past the last group (all ids -1: in-bounds rows of the token's own
   // sequence, never used), so no phase merges paths with different numbers of
   // loads in flight -- such a merge would make the compute wait for all of them.
-  int id_c[8], id_n[8], id_nn[8];
-  bf16x8 kA[2][KS], kB[2][KS];
+  int id_c[NB], id_n[NB], id_nn[NB];
+  bf16x8 kA[U][KS], kB[U][KS];
   u32x4 vA[VP], vB[VP];
-  int n_c = take8(id_c);
+  int n_c = take(id_c);
   if (n_c > 0) load_group(id_c, kA, vA);
-  int n_n = n_c > 0 ? take8(id_n) : 0;
+  int n_n = n_c > 0 ? take(id_n) : 0;
   auto rotate_ids = [&](int n_nn) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NB; ++k) {
       id_c[k] = id_n[k];
       id_n[k] = id_nn[k];
     }
@@ -320,14 +336,14 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
   };
   while (n_c > 0) {
     {
-      const int n_nn = n_n > 0 ? take8(id_nn) : 0;
+      const int n_nn = n_n > 0 ? take(id_nn) : 0;
       load_group(id_n, kB, vB);
       compute(kA, vA, id_c);
       rotate_ids(n_nn);
     }
     if (n_c == 0) break;
     {
-      const int n_nn = n_n > 0 ? take8(id_nn) : 0;
+      const int n_nn = n_n > 0 ? take(id_nn) : 0;
       load_group(id_n, kA, vA);
       compute(kB, vB, id_c);
       rotate_ids(n_nn);
@@ -360,20 +376,20 @@ __global__ void __launch_bounds__(64) qsa_kernel(const QsaParams p) {
     p.lse[(int64_t)hq * p.T + t] = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
 }
 
-template <int D>
+template <int D, int U>
 static hipError_t launch_qsa_d(const QsaParams& p, hipStream_t st) {
   const int64_t total = (int64_t)p.T * p.Hkv;
   const int64_t per = (total + kQsaXcds - 1) / kQsaXcds;
   if (per * kQsaXcds > 0x7fffffff) return hipErrorInvalidValue;
   QsaParams arg = p;
   void* args[] = {(void*)&arg};
-  return hipLaunchKernel((const void*)qsa_kernel<D>, dim3((unsigned)(per * kQsaXcds)), dim3(64),
-                         args, QsaLayout<D>::LDS_TOTAL, st);
+  return hipLaunchKernel((const void*)qsa_kernel<D, U>, dim3((unsigned)(per * kQsaXcds)), dim3(64),
+                         args, QsaLayout<D, U>::LDS_TOTAL, st);
 }
 
 hipError_t launch_qsa(const QsaParams& p, int D, hipStream_t stream) {
-  if (D == 128) return launch_qsa_d<128>(p, stream);
-  if (D == 256) return launch_qsa_d<256>(p, stream);
+  if (D == 128) return launch_qsa_d<128, 2>(p, stream);
+  if (D == 256) return launch_qsa_d<256, 1>(p, stream);
   return hipErrorInvalidValue;
 }
 
