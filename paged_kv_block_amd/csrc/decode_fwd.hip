@@ -9,7 +9,8 @@
 //
 // The path is bound by HBM bandwidth -- every live K/V byte is read once -- so
 // the design is about keeping bytes in flight on every CU until the end:
-//   * Work items are equal-size chunks: (request, chunk of CH tokens, KV head).
+//   * Work items are chunks: (request, chunk of CH tokens, KV head), every full
+//     chunk first and the partial last chunks after them.
 //     The grid is persistent (a fixed number of single-wave workgroups); wave w
 //     takes items w, w + W, w + 2W, ... of the flattened list, which it derives
 //     on the device from seq_lens (no host read), so long and short requests
@@ -58,7 +59,7 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-template <int D>
+template <int D, bool F32>
 __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
   using Lay = DecLayout<D>;
   constexpr int KS = D / 32;             // MFMA k-steps over the head dim (S^T)
@@ -74,21 +75,41 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
   const int CH = p.split_len;
   const int S = p.num_splits;
 
-  // running position in the flattened (request, chunk) list
+  // Item order: every full CH-token chunk of the batch first, then each
+  // request's partial last chunk.  Waves are dealt items round robin, so the
+  // waves that get one item more than the others mostly get a short one.
+  // Running position in the chosen (request, chunk) list:
+  int phase = 0;          // 0: full chunks, 1: partial last chunks
   int blk = 0;            // current block of 64 requests
   int blk_base = 0;       // chunks before this block
   int n_b = 0, incl = 0;  // this lane's request: chunk count, inclusive prefix in block
   auto load_block = [&]() {
     const int bb = blk * 64 + lane;
-    n_b = bb < p.B ? (p.seq_lens[bb] + CH - 1) / CH : 0;
+    int nc = 0;
+    if (bb < p.B) {
+      const int len = p.seq_lens[bb];
+      nc = phase == 0 ? len / CH : (len % CH != 0 ? 1 : 0);
+    }
+    n_b = nc;
     incl = wave_incl_scan(n_b);
   };
+  int n_full = 0;         // full chunks over the batch
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int bb = b0 + lane;
+    n_full += readlane_i32(wave_incl_scan(bb < p.B ? p.seq_lens[bb] / CH : 0), 63);
+  }
   load_block();
 
   const int W = gridDim.x;
   for (int item = blockIdx.x;; item += W) {
-    const int j = item / p.Hkv;              // flattened (request, chunk)
+    const int j = item / p.Hkv;              // position in the chunk list
     const int kvh = item - j * p.Hkv;
+    if (phase == 0 && j >= n_full) {         // on to the partial chunks
+      phase = 1;
+      blk = 0;
+      blk_base = n_full;
+      load_block();
+    }
     // advance to the block of requests that holds chunk j
     int tot = readlane_i32(incl, 63);
     while (j >= blk_base + tot && blk * 64 + 64 < p.B) {
@@ -102,15 +123,15 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
     const unsigned long long msk = __ballot(incl > local);
     const int ln = __builtin_ctzll(msk);
     const int b = blk * 64 + ln;
-    const int c = local - (readlane_i32(incl, ln) - readlane_i32(n_b, ln));
+    const int L = ld_const(p.seq_lens, b);
+    const int c = phase == 0 ? local - (readlane_i32(incl, ln) - readlane_i32(n_b, ln)) : L / CH;
 
-    const int L = p.seq_lens[b];
     // MFMA column qn is query row (token i, head h) of the request: qlen tokens
     // (one for single-token decode) x G heads, at most 16 columns.  Token i sits
     // at position L - qlen + i and, causal, sees keys [lo_i, p_i]; otherwise
     // [lo_i, L).  The item covers the union of those ranges inside its chunk.
-    const int qlen = p.qo_indptr ? p.qo_indptr[b + 1] - p.qo_indptr[b] : p.Sq;
-    const int tok0 = p.qo_indptr ? p.qo_indptr[b] : b * p.Sq;
+    const int qlen = p.qo_indptr ? ld_const(p.qo_indptr, b + 1) - ld_const(p.qo_indptr, b) : p.Sq;
+    const int tok0 = p.qo_indptr ? ld_const(p.qo_indptr, b) : b * p.Sq;
     const int qi = qn / G, qh = qn - qi * G;
     const bool col_ok = qi < qlen;
     const int p_col = L - qlen + qi;
@@ -125,7 +146,7 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
     const int t_base = k_lo & ~31;
     const int n_groups = k_hi > k_lo ? (k_hi - t_base + 31) >> 5 : 0;
     const int64_t head_off = (int64_t)kvh * p.kv_head_stride;
-    const int32_t* ids = p.kv_indices + p.kv_indptr[b];
+    const int32_t* ids = p.kv_indices + ld_const(p.kv_indptr, b);
 
     bf16x8 qf[KS];
     {
@@ -256,7 +277,7 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
       pw[2] = pack_bf16x2(sacc[1][0], sacc[1][1]);
       pw[3] = pack_bf16x2(sacc[1][2], sacc[1][3]);
       u32x4 plo = {0u, 0u, 0u, 0u};
-      if (p.out_f32) {
+      if (F32) {
         // fp32 output: P - bf16(P) enters as a second operand (~16-bit P)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -282,7 +303,7 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
         u32x4 aw;
         aw[0] = w0[0]; aw[1] = w0[1]; aw[2] = w1[0]; aw[3] = w1[1];
         oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), as_bf16x8(pw), oacc[d], 0, 0, 0);
-        if (p.out_f32)
+        if (F32)
           oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), as_bf16x8(plo), oacc[d], 0, 0, 0);
       }
       // the slab is rewritten next iteration: keep these reads before those writes
@@ -335,7 +356,7 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
         const bool empty = !(l_tot > 0.f);
         const float inv = empty ? 0.f : p.out_scale / l_tot;
         const int64_t orow = (int64_t)(tok0 + qi) * p.Hq + hq;
-        if (p.out_f32) {
+        if (F32) {
           float* o = (float*)p.out + orow * D;
 #pragma unroll
           for (int d = 0; d < DB; ++d) *(f32x4*)(o + 16 * d + 4 * g) = oacc[d] * inv;
@@ -432,8 +453,8 @@ template <int D>
 static hipError_t launch_dec(const DecodeParams& p, int grid, hipStream_t st) {
   DecodeParams arg = p;
   void* args[] = {(void*)&arg};
-  return hipLaunchKernel((const void*)decode_kernel<D>, dim3(grid), dim3(64), args,
-                         DecLayout<D>::LDS, st);
+  const void* kern = p.out_f32 ? (const void*)decode_kernel<D, true> : (const void*)decode_kernel<D, false>;
+  return hipLaunchKernel(kern, dim3(grid), dim3(64), args, DecLayout<D>::LDS, st);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int D, int grid, hipStream_t stream) {

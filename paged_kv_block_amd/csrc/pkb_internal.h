@@ -40,11 +40,11 @@ struct AttnParams {
   float out_scale;
 };
 
-// Dedicated single-token decode kernel (GQA group of at most 16 heads): a
-// persistent grid of single-wave workgroups, decode_waves_per_cu(D) per CU --
-// as many as fit at once (D = 128: two per SIMD, D = 256: one), each keeping
-// one 32-key group of loads in flight while it computes the previous one.
-constexpr int decode_waves_per_cu(int D) { return D == 128 ? 8 : 4; }
+// Dedicated decode kernel (at most 16 query rows per KV head): a persistent
+// grid of single-wave workgroups, decode_waves_per_cu(D) per CU (one per
+// SIMD), each keeping one 32-key group of loads in flight while it computes
+// the previous one.
+constexpr int decode_waves_per_cu(int) { return 4; }
 constexpr int kDecodeMaxGroup = 16;
 
 struct DecodeParams {
