@@ -597,12 +597,19 @@ attn_fwd_kernel(const AttnParams p) {
     __syncthreads();     // ... and is visible; every wave is done with tile j-1
     if (tmr[LA].M) issue_tile(tmr[LA], j + LA);   // slots of tile j-1
     if (wave_rows && tmr[0].M) {
+      // The SIMD's other wave belongs to another workgroup and is usually in a
+      // different phase: raising this wave's priority while it issues MFMAs
+      // keeps the matrix pipe fed while the other one runs its softmax.
       f32x16 sc[2];
+      __builtin_amdgcn_s_setprio(1);
       compute_s(j % Lay::NSK, sc);
+      __builtin_amdgcn_s_setprio(0);
       mask_s(tmr[0], sc);
       softmax(sc);
       rescale();
+      __builtin_amdgcn_s_setprio(1);
       compute_pv(j % Lay::NSV);
+      __builtin_amdgcn_s_setprio(0);
     }
 #pragma unroll
     for (int k = 0; k < LA; ++k) tmr[k] = tmr[k + 1];
