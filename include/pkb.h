@@ -221,7 +221,8 @@ typedef struct {
   int32_t group;
   int32_t waves, tile_m;
   int32_t n_work;           /* work items (= grid_x); each is (b, first packed row) */
-  int32_t grid_x, grid_y;
+  int32_t grid_x, grid_y;   /* (work item, KV head); launched as one 1-D grid of
+                               grid_x * grid_y workgroups, KV head fastest */
   int32_t kernel_id;
   int64_t kv_tokens;        /* sum over work items of visited KV positions */
 } pkb_prefill_plan_t;

@@ -162,7 +162,7 @@ int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
   p.out_f32 = a.out_dtype == PKB_FP32;
   p.scale_log2 = scale_or_default(sm_scale, a.D) * 1.4426950408889634f;
   p.out_scale = output_scale;
-  dim3 grid(plan->grid_x, plan->grid_y, 1);
+  dim3 grid(plan->grid_x * plan->grid_y, 1, 1);
   return hip_status(pkb::launch_attn(p, a.D, plan->waves, pkb::kModePrefill, grid,
                                      (hipStream_t)stream));
 }

@@ -124,6 +124,12 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_addr) : "m0");
 }
+// The same copy from the wave-uniform address base + byte offset off (the
+// scalar-base form: the 64-bit base sits in SGPRs, each lane adds 32 bits).
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_addr) : "m0");
+}
 
 // Lanes whose bit is set in the 64-bit scalar mask keep x, the others take y.
 __device__ __forceinline__ float select_lanes(uint64_t mask, float x, float y) {
@@ -195,8 +201,13 @@ attn_fwd_kernel(const AttnParams p) {
     bip_lo = bp[0];
     n_sel = bp[1] - bip_lo;
   } else if (MODE == kModePrefill) {
-    b = p.worklist[2 * blockIdx.x];
-    m_begin = p.worklist[2 * blockIdx.x + 1];
+    // 1-D grid, KV head fastest: the work list is longest-first, so the whole
+    // launch is dealt longest-first, and with 8 KV heads each XCD keeps one
+    // head's K/V in its L2
+    const int w = (int)blockIdx.x / p.Hkv;
+    kvh = (int)blockIdx.x - w * p.Hkv;
+    b = p.worklist[2 * w];
+    m_begin = p.worklist[2 * w + 1];
     tok_base = p.qo_indptr[b];
     qlen = p.qo_indptr[b + 1] - tok_base;
     m_end = min(m_begin + TILE_M, qlen * G);
@@ -377,10 +388,11 @@ attn_fwd_kernel(const AttnParams p) {
       const int t = tm.tsrc[lc];
       const int key = i * Lay::KPI + lane / Lay::LPK;
       const int r = key & 7;
-      const int rr = (t + r < L) ? r : 0;
       const int pp = lane % Lay::LPK;
-      lds_dma16(p.k + tm.src[lc] + rr * D + (pp ^ (key & 15)) * 8, kst + i * 1024);
-      lds_dma16(p.v + tm.src[lc] + rr * D + v_unswz(key, pp) * 8, vst + i * 1024);
+      // rows past the sequence end read the chunk's first row instead
+      const uint32_t row = (t + r < L) ? (uint32_t)(r * D * 2) : 0u;
+      lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst + i * 1024);
+      lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst + i * 1024);
     }
   };
 
