@@ -376,7 +376,8 @@ int bsa_sage_validate(const int32_t* q2k_block_index_h, int32_t capacity,
 
 /* Trusted run (MHA, D = 128, 64-token blocks).
  *   q [B,H,Sq,128] int8, k [B,H,Sk,128] int8,
- *   v_fp8 [B,H,128,ceil(Sk/64)*64] OCP E4M3FN in HDS layout (tokens contiguous),
+ *   v_fp8 [B,H,128,ceil(Sk/64)*64] OCP E4M3FN in HDS layout (tokens contiguous);
+ *   Sk above 2^25 returns PKB_ERR_UNSUPPORTED (32-bit offsets inside one head),
  *   q_scale [B,H,ceil(Sq/128)*4] (one per 32 rows), k_scale [B,H,ceil(Sk/64)],
  *   v_scale [B,H,128] fp32;
  *   q2k_block_index [B,H,ceil(Sq/64),capacity] int32;

@@ -382,6 +382,7 @@ int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
     return PKB_ERR_ARG;
   if (capacity > 0 && !q2k_block_index) return PKB_ERR_ARG;
   if ((int64_t)B * H * cdiv(Sq, 64) > 0x7fffffff) return PKB_ERR_UNSUPPORTED;
+  if (Sk > (1 << 25)) return PKB_ERR_UNSUPPORTED;   // V offsets inside one head fit 32 bits
   pkb::SageParams p;
   memset(&p, 0, sizeof(p));
   p.q = (const int8_t*)q_int8;

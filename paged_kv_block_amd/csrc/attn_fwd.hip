@@ -107,6 +107,14 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2e));
 }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+// Written as inline assembly: with the builtin, the compiler has been seen to
+// read the same element of a packed register quad for all four pairs.
+__device__ __forceinline__ float dot2_bf16_ones(uint32_t pk, float acc) {
+  asm("v_dot2c_f32_bf16_e32 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(pk));
+  return acc;
+}
+
 // Waits until at most N of this wave's vector-memory operations are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -381,18 +389,35 @@ attn_fwd_kernel(const AttnParams p) {
   auto issue_tile = [&](const TM& tm, int j) {
     const uint32_t kst = lds_base + (j % Lay::NSK) * Lay::TILE_B;
     const uint32_t vst = lds_base + Lay::V_BASE + (j % Lay::NSV) * Lay::TILE_B;
+    // rows past the sequence end read their chunk's first row instead; the
+    // per-row test is needed only when one of this wave's chunks is partial
+    bool whole = true;
 #pragma unroll
-    for (int ii = 0; ii < IPW; ++ii) {
-      const int i = wave * IPW + ii;
-      const int lc = (ii * Lay::KPI) >> 3;   // = chunk (i * KPI) / 8 - wave * CPW
-      const int t = tm.tsrc[lc];
-      const int key = i * Lay::KPI + lane / Lay::LPK;
-      const int r = key & 7;
-      const int pp = lane % Lay::LPK;
-      // rows past the sequence end read the chunk's first row instead
-      const uint32_t row = (t + r < L) ? (uint32_t)(r * D * 2) : 0u;
-      lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst + i * 1024);
-      lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst + i * 1024);
+    for (int lc = 0; lc < CPW; ++lc) whole = whole && (tm.tsrc[lc] + 8 <= L);
+    if (whole) {
+#pragma unroll
+      for (int ii = 0; ii < IPW; ++ii) {
+        const int i = wave * IPW + ii;
+        const int lc = (ii * Lay::KPI) >> 3;   // = chunk (i * KPI) / 8 - wave * CPW
+        const int key = i * Lay::KPI + lane / Lay::LPK;
+        const uint32_t row = (uint32_t)((key & 7) * D * 2);
+        const int pp = lane % Lay::LPK;
+        lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst + i * 1024);
+        lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < IPW; ++ii) {
+        const int i = wave * IPW + ii;
+        const int lc = (ii * Lay::KPI) >> 3;
+        const int t = tm.tsrc[lc];
+        const int key = i * Lay::KPI + lane / Lay::LPK;
+        const int r = key & 7;
+        const int pp = lane % Lay::LPK;
+        const uint32_t row = (t + r < L) ? (uint32_t)(r * D * 2) : 0u;
+        lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst + i * 1024);
+        lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst + i * 1024);
+      }
     }
   };
 
@@ -556,8 +581,13 @@ attn_fwd_kernel(const AttnParams p) {
       for (int t = 0; t < 4; ++t) {
         const float e0 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t], sl2, -m_use));
         const float e1 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t + 1], sl2, -m_use));
-        psum += e0 + e1;
-        w[t] = cvt_pk_bf16(e0, e1);
+        const uint32_t pk = cvt_pk_bf16(e0, e1);
+        w[t] = pk;
+        // the row sum adds the probabilities as rounded for the PV product
+        // (bf16 output), or exactly (fp32 output, which also multiplies the
+        // rounding remainders)
+        if (F32) psum += e0 + e1;
+        else psum = dot2_bf16_ones(pk, psum);
         if (F32)
           wl4[t] = cvt_pk_bf16(e0 - __uint_as_float(w[t] << 16), e1 - __uint_as_float(w[t] & 0xFFFF0000u));
       }

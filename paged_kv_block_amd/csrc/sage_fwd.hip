@@ -72,9 +72,14 @@ __device__ __forceinline__ int sage_key_of_row(int rho) {
   return 32 * h + 16 * kb + 4 * a + c;
 }
 
-__device__ __forceinline__ void sage_dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_addr) : "m0");
+// 16 bytes per lane from the wave-uniform address base + byte offset off to
+// LDS address lds_addr + 16 * lane (global_load_lds_dwordx4 in its scalar-base
+// form; the LDS base is taken from M0, which needs one wait state after the
+// SALU write).  Inline assembly keeps the compiler from ordering later LDS
+// reads after every copy in flight: the kernel orders them itself.
+__device__ __forceinline__ void sage_dma16(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_addr) : "m0");
 }
 
 template <int N>
@@ -133,17 +138,21 @@ sage_kernel(const SageParams p) {
   auto issue_block = [&](const BlockMeta& m, int t) {
     const uint32_t kst = lds_base + (t % kNStage) * kStage;
     const uint32_t vst = kst + kKTile;
+    const int8_t* kb = p.k + (bh * p.Sk + m.beta * 64) * 128;
+    const uint8_t* vb = p.v + bh * 128 * p.Skp + m.beta * 64;
+    // the per-key test is needed only for a block that ends past Sk
+    const bool whole = m.beta * 64 + 64 <= p.Sk;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = wave * 4 + ii;
       const int rho = 8 * i + (lane >> 3);
       const int kp = (lane & 7) ^ ((rho >> 1) & 7);
       int key = sage_key_of_row(rho);
-      if (m.beta * 64 + key >= p.Sk) key = 0;
-      sage_dma16(p.k + ((bh * p.Sk + m.beta * 64 + key) * 128 + kp * 16), kst + i * 1024);
+      if (!whole && m.beta * 64 + key >= p.Sk) key = 0;
+      sage_dma16(kb, (uint32_t)(key * 128 + kp * 16), kst + i * 1024);
       const int d = 16 * i + (lane >> 2);
       const int vp = (lane & 3) ^ ((d >> 2) & 3);
-      sage_dma16(p.v + ((bh * 128 + d) * p.Skp + m.beta * 64 + vp * 16), vst + i * 1024);
+      sage_dma16(vb, (uint32_t)(d * p.Skp + vp * 16), vst + i * 1024);
     }
   };
 

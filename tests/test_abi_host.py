@@ -415,6 +415,21 @@ def test_sage_validate_matches_spec():
         assert got == want, (t, got, want)
 
 
+def test_sage_run_static_errors():
+    # Rejected before any device work: the dummy pointers are never dereferenced.
+    L = P.lib()
+    d = ctypes.c_void_p(256)
+
+    def run(B=1, H=1, Sq=64, Sk=64, q=d, mask=M.DENSE):
+        return L.bsa_sage_run(q, d, d, d, d, d, d, 1, 1, None, 0, None, 0, 0,
+                              B, H, Sq, Sk, 0.0, mask, d, None, None)
+    assert run(q=None) == M.PKB_ERR_ARG
+    assert run(Sk=0) == M.PKB_ERR_ARG
+    assert run(mask=7) == M.PKB_ERR_ARG
+    # V^T offsets inside one head are 32-bit: Sk up to 2^25
+    assert run(Sk=(1 << 25) + 1) == M.PKB_ERR_UNSUPPORTED
+
+
 # ----------------------------------------------------------------------------- QSA
 
 def test_qsa_validate_matches_spec():
