@@ -22,7 +22,9 @@
 // contiguous [8, D] slab of the HND pool.  Tiles go HBM -> LDS through
 // direct-to-LDS loads (global_load_lds_dwordx4: 1 KB per wave instruction, no
 // registers) into a K ring and a V ring, one or two tiles ahead of use, with
-// one workgroup barrier per tile.  Rows are stored unpadded with their 16-byte
+// one workgroup barrier per tile.  Each copy takes its chunk's pool address
+// from SGPRs plus a per-lane 32-bit offset fixed per instruction, so issuing a
+// tile's copies needs no vector ALU work.  Rows are stored unpadded with their 16-byte
 // pieces permuted per row: K piece l sits at l ^ (key & 15), so the A-operand
 // reads of 16 consecutive keys hit distinct banks; the V permutation (v_swz)
 // spreads the four 16-lane groups of a transpose read over all 64 banks.
