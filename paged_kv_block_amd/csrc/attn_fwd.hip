@@ -297,15 +297,25 @@ attn_fwd_kernel(const AttnParams p) {
     const int qq = v >> cpb_sh;
     return ld_const(p.block_indices, bip_lo + qq) * p.kvbs + (v - (qq << cpb_sh)) * 8;
   };
-  // element offset of token t's row in the K (V) pool
-  auto token_src = [&](int t) -> int64_t {
-    const int pi = ps_pow2 ? (t >> ps_sh) : t / p.page_size;
-    const int slot = t - pi * p.page_size;
-    return (int64_t)ld_const(ids, pi) * p.kv_page_stride + head_off + (int64_t)slot * D;
-  };
 
   constexpr int CPW = 8 / NW;
   using TM = TileMeta<CPW>;
+  // pool offsets of the chunks this wave copies (tm.tsrc set)
+  auto fill_src = [&](TM& tm) {
+    int pi[CPW], id[CPW];
+#pragma unroll
+    for (int lc = 0; lc < CPW; ++lc) pi[lc] = ps_pow2 ? (tm.tsrc[lc] >> ps_sh) : tm.tsrc[lc] / p.page_size;
+    // (consecutive chunks usually share a page: one load then serves both)
+#pragma unroll
+    for (int lc = 0; lc < CPW; ++lc) {
+      if (lc > 0 && pi[lc] == pi[lc - 1]) id[lc] = id[lc - 1];
+      else id[lc] = ld_const(ids, pi[lc]);
+    }
+#pragma unroll
+    for (int lc = 0; lc < CPW; ++lc)
+      tm.src[lc] = (int64_t)id[lc] * p.kv_page_stride + head_off +
+                   (int64_t)(tm.tsrc[lc] - pi[lc] * p.page_size) * D;
+  };
   auto tile_meta = [&](int j) -> TM {
     TM tm;
     if (CONTIG) {
@@ -342,10 +352,9 @@ attn_fwd_kernel(const AttnParams p) {
         for (int lc = 0; lc < CPW; ++lc) {
           const int c = wave * CPW + lc;
           const bool in_range = (M_range >> (8 * c)) & 0xFFu;
-          const int t = in_range ? t0 + 8 * c : t_r;
-          tm.tsrc[lc] = t;
-          tm.src[lc] = token_src(t);
+          tm.tsrc[lc] = in_range ? t0 + 8 * c : t_r;
         }
+        fill_src(tm);
       }
     } else {
       uint64_t M = 0;
@@ -376,10 +385,9 @@ attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
         for (int lc = 0; lc < CPW; ++lc) {
           const int c = wave * CPW + lc;
-          const int t = ((M >> (8 * c)) & 0xFFu) ? small_chunk_token(j * 8 + c) : t_first;
-          tm.tsrc[lc] = t;
-          tm.src[lc] = token_src(t);
+          tm.tsrc[lc] = ((M >> (8 * c)) & 0xFFu) ? small_chunk_token(j * 8 + c) : t_first;
         }
+        fill_src(tm);
       }
     }
     return tm;
