@@ -25,8 +25,11 @@
 //     lane half h's accumulator holds keys 32h .. 32h+31 in order;
 //   * the int32 scores are scaled once per (wave, block): q_scale is constant
 //     over a wave's 32 rows and k_scale over the block;
-//   * online softmax in base 2 with the exact running max (P <= 1, so P * 448
-//     keeps E4M3's range for the small weights); P is packed to OCP E4M3
+//   * online softmax in base 2 whose reference moves only when a row max
+//     passes it by more than 2 (so the rescale of O is rare and P <= 4); the
+//     exponent carries log2(112), so the exp returns P * 112 <= 448, inside
+//     E4M3's range; blocks that no row of the wave cuts skip the key mask;
+//     P * 112 is packed to OCP E4M3
 //     (v_cvt_pk_fp8_f32) as a hi part plus the rounding residual -- E4M3 alone
 //     keeps 3 mantissa bits, too coarse for rows with only a few admitted keys;
 //   * V arrives in HDS layout (tokens contiguous per head dim), which is the
@@ -34,7 +37,8 @@
 //     lane half h reads the 32 contiguous bytes of keys 32h .. 32h+31, the
 //     same keys (in the same order) its P^T operand holds.  Keys at or past a
 //     partial block's size are zeroed in LDS (their storage may hold NaN codes);
-//   * the epilogue applies v_scale[d] / (448 l) and writes bf16.
+//   * the epilogue applies v_scale[d] / l (O and l both carry the factor 112)
+//     and writes bf16.
 // Workgroups are dealt round-robin over the 8 XCDs; each XCD gets a contiguous
 // run of (head, query block) items so the K/V of the heads it works on stay in
 // its L2.
@@ -53,7 +57,11 @@ constexpr int kNStage = 2;
 static_assert(kNStage >= 2 && kNStage <= 4, "wait counts cover up to two blocks in flight");
 constexpr int kLA = kNStage - 1;           // blocks copied ahead of the one computed
 constexpr int kLds = kNStage * kStage;     // 32 KB: four workgroups (two waves per SIMD) per CU
-constexpr float kP8 = 448.f;               // P * 448 is stored (E4M3 max 448)
+// The softmax reference only moves when a row max passes it by more than
+// kSlack (log2 units), so P <= 2^kSlack; P * kP8 <= 448, the E4M3 maximum.
+constexpr float kSlack = 2.f;
+constexpr float kP8 = 112.f;
+constexpr float kLog2P8 = 6.807354922057604f;   // log2(112)
 constexpr int kXcds = 8;
 }  // namespace
 
@@ -260,23 +268,37 @@ sage_kernel(const SageParams p) {
       float mx = -INFINITY;
       int kvh = kv - 32 * hh;        // keys of this lane half below the block size
       if (p.causal) kvh = min(kvh, p_row - bm[0].beta * 64 - 32 * hh + 1);
+      if (__builtin_amdgcn_ballot_w64(kvh < 32)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = (16 * kb + i < kvh) ? (float)sacc[kb][i] * sc : -INFINITY;
-          sv[kb][i] = x;
-          mx = fmaxf(mx, x);
-        }
+          for (int i = 0; i < 16; ++i) {
+            const float x = (16 * kb + i < kvh) ? (float)sacc[kb][i] * sc : -INFINITY;
+            sv[kb][i] = x;
+            mx = fmaxf(mx, x);
+          }
+      } else {
+        // every key of the block is admitted in every row of the wave
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float x = (float)sacc[kb][i] * sc;
+            sv[kb][i] = x;
+            mx = fmaxf(mx, x);
+          }
+      }
       mx = half_max(mx);
-      const float m_ref = fmaxf(m_run, mx);
+      const float m_ref = (mx > m_run + kSlack) ? mx : m_run;
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      // P * kP8 straight from the exponent: exp2(s - m + log2 kP8)
+      const float m_p8 = m_use - kLog2P8;
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(sv[kb][i] - m_use);
+          const float e = fast_exp2(sv[kb][i] - m_p8);
           sv[kb][i] = e;
           psum += e;
         }
@@ -290,14 +312,14 @@ sage_kernel(const SageParams p) {
       }
       l_run += psum;
       m_run = m_ref;
-      // ---- P^T -> fp8 (x 448) as hi + lo parts, slot j = 16kb + i ----
+      // ---- P^T * kP8 -> fp8 as hi + lo parts, slot j = 16kb + i ----
       i32x8 pb, pl;
 #pragma unroll
       for (int wd = 0; wd < 8; ++wd) {
         const int kb = wd >> 2;
         const int i0 = 4 * (wd & 3);
-        const float x0 = sv[kb][i0] * kP8, x1 = sv[kb][i0 + 1] * kP8;
-        const float x2 = sv[kb][i0 + 2] * kP8, x3 = sv[kb][i0 + 3] * kP8;
+        const float x0 = sv[kb][i0], x1 = sv[kb][i0 + 1];
+        const float x2 = sv[kb][i0 + 2], x3 = sv[kb][i0 + 3];
         int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
         const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
@@ -320,12 +342,12 @@ sage_kernel(const SageParams p) {
     if (t + 1 + kLA < n) bm[kLA] = block_meta(t + 1 + kLA);
   }
 
-  // ---- epilogue: O = O^T * v_scale[d] / (448 l) -> bf16 [B, H, Sq, 128] ----
+  // ---- epilogue: O = O^T * v_scale[d] / l -> bf16 [B, H, Sq, 128] ----
   const float l_tot = half_sum(l_run);
   if (!row_ok) return;
-  const float inv = l_tot > 0.f ? 1.f / (kP8 * l_tot) : 0.f;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // O and l both carry kP8
   if (p.lse && hh == 0)
-    p.lse[bh * p.Sq + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    p.lse[bh * p.Sq + row] = l_tot > 0.f ? (m_run + __log2f(l_tot) - kLog2P8) * kLn2 : -INFINITY;
   const float* vsc = p.v_scale + bh * 128;
   uint16_t* o = p.out + (bh * p.Sq + row) * 128;
 #pragma unroll
