@@ -87,23 +87,38 @@ def dev_i32(a):
     return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).cuda()
 
 
+WARMUP_MIN_S = 0.2   # untimed warmup keeps going until this much wall time has passed
+
+
 def time_launches(fn, steps, warmup):
-    """Run fn() warmup times, then `steps` times with per-launch events.
+    """Run fn() at least `warmup` times, and on until WARMUP_MIN_S of untimed
+    work has run (the engine clock ramps up over the first tens of ms of
+    sustained load; timed right after a few calls, a kernel reads up to 10%
+    slow).  Then time `steps` back-to-back calls between two events (the step
+    time: nothing else is enqueued between the launches), then `steps` more
+    calls each bracketed by its own events (the mean launch duration).
     Returns (total_ms / steps, mean per-launch ms)."""
+    t_start = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    while time.perf_counter() - t_start < WARMUP_MIN_S:
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
     for a, b in evs:
         a.record()
         fn()
         b.record()
-    t1.record()
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in evs]
     return t0.elapsed_time(t1) / steps, float(np.mean(per))
@@ -454,7 +469,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed steps before each timed region (at least this many, and "
+                         "on until 0.2 s of untimed work has run)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["decode", "decode_q", "bsa", "prefill", "prefill256", "tiny",
