@@ -293,11 +293,11 @@ def prefill_plan_capacity(args, max_qlen):
 # Decode
 # ----------------------------------------------------------------------------
 
-def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus):
+def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, per_wave=8):
     """Chunk (split) policy from the static maximum length: chunk length CH
     starts at 1024 tokens (doubled while a request would need > 4096 chunks),
-    then halves down to 64 until B*Hkv*ceil(max_seq_len/CH) >= 8 items per
-    persistent wave (4 waves per CU).  Returns (status, bytes, chunks, CH)."""
+    then halves down to 64 until B*Hkv*ceil(max_seq_len/CH) >= per_wave items
+    per persistent wave (4 waves per CU).  Returns (status, bytes, chunks, CH)."""
     if min(B, Hq, Hkv, num_cus) < 1 or page_size < 1:
         return PKB_ERR_ARG, 0, 0, 0
     if Hq % Hkv:
@@ -310,7 +310,7 @@ def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus):
     while cdiv(max_seq_len, CH) > 4096:
         CH *= 2
     waves = 4 * num_cus
-    while CH > 64 and B * Hkv * cdiv(max_seq_len, CH) < 8 * waves:
+    while CH > 64 and B * Hkv * cdiv(max_seq_len, CH) < per_wave * waves:
         CH //= 2
     S = cdiv(max_seq_len, CH)
     split_len = CH
@@ -333,10 +333,12 @@ def decode_validate(B, P, ps, max_seq_len, kv_indptr, kv_indices, seq_lens):
 
 
 def decode_q_policy(B, max_q, Hq, Hkv, D, max_seq_len, page_size, num_cus):
-    """Multi-token decode: the same chunk policy; partials [B, max_q, Hq, S, D+4]."""
+    """Multi-token decode: the same chunk policy, aiming at 4 items per wave
+    when max_q > 1; partials [B, max_q, Hq, S, D+4]."""
     if max_q < 1:
         return PKB_ERR_ARG, 0, 0, 0
-    st, nbytes, S, CH = decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus)
+    st, nbytes, S, CH = decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus,
+                                      4 if max_q > 1 else 8)
     if st != PKB_OK:
         return st, 0, 0, 0
     return PKB_OK, nbytes * max_q, S, CH

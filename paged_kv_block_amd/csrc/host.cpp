@@ -310,26 +310,35 @@ int paged_prefill_plan_capacity(const prefill_static_args* a, int32_t max_qlen,
 
 // ------------------------------------------------------------------ decode
 
-int paged_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
-                                int32_t max_seq_len, int32_t page_size, int32_t num_cus,
-                                size_t* bytes, int32_t* num_splits, int32_t* split_len) {
+// Chunk length CH (tokens per work item): start at 1024 (grown while a request
+// would need more than 4096 chunks), then halve down to 64 until the largest
+// possible item count reaches per_wave items per persistent wave (4 waves per
+// CU).  Multi-token decode aims at 4 items per wave: its merge reads max_q
+// times more partials, so fewer, longer chunks pay off there.
+static int decode_split(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len,
+                        int32_t page_size, int32_t num_cus, int per_wave, size_t* bytes,
+                        int32_t* num_splits, int32_t* split_len) {
   if (B < 1 || Hq < 1 || Hkv < 1 || num_cus < 1 || page_size < 1) return PKB_ERR_ARG;
   if (Hq % Hkv) return PKB_ERR_SHAPE;
   if ((D != 128 && D != 256) || page_size % 8) return PKB_ERR_UNSUPPORTED;
   if (max_seq_len < 1 || max_seq_len > PKB_MAX_SEQ_LEN) return PKB_ERR_ARG;
-  // Chunk length CH (tokens per work item): start at 1024 (grown while a request
-  // would need more than 4096 chunks), then halve down to 64 until the largest
-  // possible item count reaches 8 items per persistent wave (4 waves per CU).
   int64_t CH = 1024;
   while (cdiv(max_seq_len, CH) > 4096) CH *= 2;
   const int64_t waves = 4LL * num_cus;
-  while (CH > 64 && (int64_t)B * Hkv * cdiv(max_seq_len, CH) < 8 * waves) CH /= 2;
+  while (CH > 64 && (int64_t)B * Hkv * cdiv(max_seq_len, CH) < per_wave * waves) CH /= 2;
   const int64_t S = cdiv(max_seq_len, CH);
   if (num_splits) *num_splits = (int32_t)S;
   if (split_len) *split_len = (int32_t)CH;
   // fp32 partials [B, Hq, S, D+4]: unnormalised O, running max, running sum, pad.
   if (bytes) *bytes = S == 1 ? 0 : (size_t)B * Hq * S * (D + 4) * sizeof(float);
   return PKB_OK;
+}
+
+int paged_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t max_seq_len, int32_t page_size, int32_t num_cus,
+                                size_t* bytes, int32_t* num_splits, int32_t* split_len) {
+  return decode_split(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, 8, bytes, num_splits,
+                      split_len);
 }
 
 int paged_decode_validate(int32_t B, int32_t num_pages, int32_t page_size, int32_t max_seq_len,
@@ -351,8 +360,8 @@ int paged_decode_q_workspace_size(int32_t B, int32_t max_q, int32_t Hq, int32_t 
                                   size_t* bytes, int32_t* num_splits, int32_t* split_len) {
   if (max_q < 1) return PKB_ERR_ARG;
   size_t one = 0;
-  int st = paged_decode_workspace_size(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, &one,
-                                       num_splits, split_len);
+  int st = decode_split(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, max_q > 1 ? 4 : 8, &one,
+                        num_splits, split_len);
   if (st) return st;
   // fp32 partials [B, max_q, Hq, S, D+4]
   if (bytes) *bytes = one * (size_t)max_q;
