@@ -377,9 +377,12 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
 }
 
 // Merge of one (request, query token, query head): LSE-weighted sum of its live
-// splits' partials.  Lane s holds split s's (m, l) (64 splits per pass), so the max and
-// the weights take one load round trip; the O accumulation then issues the
-// partial rows of eight splits at a time, each lane owning D/64 dims.
+// splits' partials, each lane owning D/64 dims.  Up to kMergeFew splits, all
+// loads go out in one round.  Beyond that, lane s holds split s's (m, l) (64
+// splits per pass), so the max and the weights take one load round trip, and
+// the O accumulation then issues the partial rows of eight splits at a time.
+constexpr int kMergeFew = 16;   // split counts merged with a single round of loads
+
 template <int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(const MergeParams p) {
   constexpr int PER = D / 64;
@@ -395,42 +398,74 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(const MergeParams p) {
   const int n = min(p.num_splits, (L + p.split_len - 1) / p.split_len);
   const float* base = p.part + (int64_t)blockIdx.x * p.num_splits * ROW;
   float M = -INFINITY;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int s = s0 + lane;
-    float m = s < n ? base[(int64_t)s * ROW + D] : -INFINITY;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    M = fmaxf(M, m);
-  }
   float lsum = 0.f;
   float acc[PER];
 #pragma unroll
   for (int t = 0; t < PER; ++t) acc[t] = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < n; s0 += 64) {
-      const int s = s0 + lane;
-      float w = 0.f, wl = 0.f;
-      if (s < n) {
-        w = fast_exp2(base[(int64_t)s * ROW + D] - M);
-        wl = w * base[(int64_t)s * ROW + D + 1];
-      }
+  if (n <= kMergeFew) {
+    // Few splits: every load is issued in one round (lane s < n reads split
+    // s's (m, l); each lane reads its dims of every partial row), then the
+    // max, the weights and the weighted sum follow from registers.
+    float m = -INFINITY, l = 0.f;
+    if (lane < n) {
+      m = base[(int64_t)lane * ROW + D];
+      l = base[(int64_t)lane * ROW + D + 1];
+    }
+    float x[kMergeFew][PER];
+#pragma unroll
+    for (int k = 0; k < kMergeFew; ++k)
+#pragma unroll
+      for (int t = 0; t < PER; ++t) x[k][t] = k < n ? base[(int64_t)k * ROW + lane * PER + t] : 0.f;
+    M = m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (M != -INFINITY) {
+      const float w = lane < n ? fast_exp2(m - M) : 0.f;
+      float wl = w * l;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) wl += __shfl_xor(wl, o);
-      lsum += wl;
-      const int cnt = min(64, n - s0);
-      for (int k0 = 0; k0 < cnt; k0 += 8) {
-        float x[8][PER];
+      lsum = wl;
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+      for (int k = 0; k < kMergeFew; ++k) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
 #pragma unroll
-          for (int t = 0; t < PER; ++t)
-            x[k][t] = (k0 + k < cnt) ? base[(int64_t)(s0 + k0 + k) * ROW + lane * PER + t] : 0.f;
+        for (int t = 0; t < PER; ++t) acc[t] += wk * x[k][t];
+      }
+    }
+  } else {
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const int s = s0 + lane;
+      float m = s < n ? base[(int64_t)s * ROW + D] : -INFINITY;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          // k0 + k <= 63: k0 < cnt <= 64 steps by 8
-          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k0 + k));
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      M = fmaxf(M, m);
+    }
+    if (M != -INFINITY) {
+      for (int s0 = 0; s0 < n; s0 += 64) {
+        const int s = s0 + lane;
+        float w = 0.f, wl = 0.f;
+        if (s < n) {
+          w = fast_exp2(base[(int64_t)s * ROW + D] - M);
+          wl = w * base[(int64_t)s * ROW + D + 1];
+        }
 #pragma unroll
-          for (int t = 0; t < PER; ++t) acc[t] += wk * x[k][t];
+        for (int o = 32; o >= 1; o >>= 1) wl += __shfl_xor(wl, o);
+        lsum += wl;
+        const int cnt = min(64, n - s0);
+        for (int k0 = 0; k0 < cnt; k0 += 8) {
+          float x[8][PER];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int t = 0; t < PER; ++t)
+              x[k][t] = (k0 + k < cnt) ? base[(int64_t)(s0 + k0 + k) * ROW + lane * PER + t] : 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            // k0 + k <= 63: k0 < cnt <= 64 steps by 8
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k0 + k));
+#pragma unroll
+            for (int t = 0; t < PER; ++t) acc[t] += wk * x[k][t];
+          }
         }
       }
     }
