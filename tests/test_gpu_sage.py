@@ -170,3 +170,22 @@ def test_sage_contiguous_fast_path():
     junk[..., 1:] = rng.integers(-100, 100, size=junk[..., 1:].shape)
     out_j, _ = _run_ext(case, index=junk, contiguous=True)
     assert torch.equal(out_c, out_j)
+
+
+def test_sage_growing_scores():
+    """Every row visits its blocks in order and each block's keys are scaled
+    12% above the previous one's, so the running row max keeps rising through
+    the walk: some rises stay inside the kernel's rescale slack and others pass
+    it (the running output is then rescaled).  Output and LSE stay on the bar."""
+    nkb = 16
+    case = W.make_sage(46, 1, 2, 128, 64 * nkb, cap=nkb, nsel=nkb, per_row_counts=False,
+                       block_sizes_rank=0)
+    case.q2k_block_index[:] = np.arange(nkb, dtype=np.int32)
+    grow = torch.tensor([1.12 ** blk for blk in range(nkb)], dtype=torch.float32)
+    case.k_scale = (case.k_scale * grow).contiguous()
+    case.softmax_scale = 0.3
+    _say("sage growing scores")
+    out, lse = _run_ext(case)
+    ref_o, ref_l = _oracle_ext(case)
+    assert_close(f64(out), ref_o, TOL_SAGE, "out")
+    assert_close(f64(lse), ref_l, 2e-3, "lse")
