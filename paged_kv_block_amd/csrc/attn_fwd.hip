@@ -109,14 +109,6 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2e));
 }
 
-// acc + lo + hi of a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
-// Written as inline assembly: with the builtin, the compiler has been seen to
-// read the same element of a packed register quad for all four pairs.
-__device__ __forceinline__ float dot2_bf16_ones(uint32_t pk, float acc) {
-  asm("v_dot2c_f32_bf16_e32 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(pk));
-  return acc;
-}
-
 // Waits until at most N of this wave's vector-memory operations are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -591,13 +583,8 @@ attn_fwd_kernel(const AttnParams p) {
       for (int t = 0; t < 4; ++t) {
         const float e0 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t], sl2, -m_use));
         const float e1 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t + 1], sl2, -m_use));
-        const uint32_t pk = cvt_pk_bf16(e0, e1);
-        w[t] = pk;
-        // the row sum adds the probabilities as rounded for the PV product
-        // (bf16 output), or exactly (fp32 output, which also multiplies the
-        // rounding remainders)
-        if (F32) psum += e0 + e1;
-        else psum = dot2_bf16_ones(pk, psum);
+        psum += e0 + e1;
+        w[t] = cvt_pk_bf16(e0, e1);
         if (F32)
           wl4[t] = cvt_pk_bf16(e0 - __uint_as_float(w[t] << 16), e1 - __uint_as_float(w[t] & 0xFFFF0000u));
       }

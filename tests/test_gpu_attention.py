@@ -165,6 +165,27 @@ def test_prefill_sweep(i):
     assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
 
 
+def test_prefill_growing_scores():
+    """Key magnitudes grow along each request (row t scaled by 1 + t/50), so
+    the running row max keeps rising: rises past the kernel's rescale slack
+    rescale the running output, smaller ones keep the old reference."""
+    case = W.make_prefill(470, 2, [64, 200], [900, 300], 8, 2, 128, 16, mask="causal",
+                          extra_pages=2)
+    ps = case.k.shape[2]
+    k = case.k.float()
+    for b, L in enumerate(case.seq_lens):
+        for t in range(int(L)):
+            k[int(case.block_tables[b, t // ps]), :, t % ps, :] *= 1.0 + t / 50.0
+    case.k = k.to(torch.bfloat16)
+    _say("prefill growing scores")
+    out, lse = run_prefill(case)
+    ref_o, ref_l = oracle_prefill(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, _ = run_prefill(case, out_dtype=torch.float32, with_lse=False)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
+
+
 @pytest.mark.parametrize("D,w", [(128, -1), (128, 1024), (256, -1)])
 def test_batch_prefill_sampled(D, w):
     case = W.batch_prefill(3, D=D, window_left=w)
