@@ -133,11 +133,12 @@ __device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint
                :: "v"(off), "s"(base), "s"(lds_addr) : "m0");
 }
 
-// Lanes whose bit is set in the 64-bit scalar mask keep x, the others take y.
+// Lanes whose bit is set in the 64-bit scalar mask keep x, the others take y
+// (one v_cndmask with the mask as its condition; written with the inverse
+// ballot so that the compiler sees the read of x, which may be an MFMA result
+// still in flight, and inserts the wait states it needs).
 __device__ __forceinline__ float select_lanes(uint64_t mask, float x, float y) {
-  float r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(y), "v"(x), "s"(mask));
-  return r;
+  return __builtin_amdgcn_inverse_ballot_w64(mask) ? x : y;
 }
 
 // Slack of the softmax reference max, in log2 units.
