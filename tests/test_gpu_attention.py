@@ -212,6 +212,26 @@ DECODE_SWEEP = [
 ]
 
 
+def test_decode_growing_scores():
+    """Key magnitudes grow along each request (row t scaled by 1 + t/100), so
+    every split's running max keeps rising and its output is rescaled often;
+    the merge then combines splits whose maxima differ widely."""
+    case = W.make_decode(560, 3, 16, 4, 128, [3000, 700, 1500], 16, extra_pages=2)
+    ps = case.k.shape[2]
+    k = case.k.float()
+    for b, L in enumerate(case.seq_lens):
+        pages = case.kv_indices[case.kv_indptr[b]:case.kv_indptr[b + 1]]
+        for t in range(int(L)):
+            k[int(pages[t // ps]), :, t % ps, :] *= 1.0 + t / 100.0
+    case.k = k.to(torch.bfloat16)
+    _say("decode growing scores")
+    out, lse, S = run_decode(case, num_cus=16)
+    assert S > 1
+    ref_o, ref_l = oracle_decode(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+
+
 @pytest.mark.parametrize("i", range(len(DECODE_SWEEP)))
 def test_decode_sweep(i):
     B, Hq, Hkv, D, sl, ps, mask, w, ncu = DECODE_SWEEP[i]
