@@ -533,16 +533,20 @@ attn_fwd_kernel(const AttnParams p) {
   auto mask_s = [&](const TM& tm, f32x16 (&acc)[2]) {
     auto chunk_t = [&](int c) { return CONTIG ? tm.t0 + 8 * c : tm.ts[c]; };
     if (tm.M != ~0ull) {
-      // lanes 0-31 take key bit pos, lanes 32-63 bit pos + 4: a scalar lane mask
+      // lanes 0-31 take key bit pos, lanes 32-63 bit pos + 4: a scalar lane
+      // mask whose halves are those bits sign-extended (one bit-field extract
+      // each)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t word = (uint32_t)(tm.M >> (32 * kb));
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int pos = 32 * kb + 8 * (i >> 2) + (i & 3);
-          const uint64_t lo = ((tm.M >> pos) & 1) ? 0xFFFFFFFFull : 0ull;
-          const uint64_t hi = ((tm.M >> (pos + 4)) & 1) ? 0xFFFFFFFF00000000ull : 0ull;
-          acc[kb][i] = select_lanes(lo | hi, acc[kb][i], neg_inf);
+          const int pw = 8 * (i >> 2) + (i & 3);
+          const uint32_t lo = (uint32_t)((int32_t)(word << (31 - pw)) >> 31);
+          const uint32_t hi = (uint32_t)((int32_t)(word << (27 - pw)) >> 31);
+          acc[kb][i] = select_lanes((uint64_t)lo | ((uint64_t)hi << 32), acc[kb][i], neg_inf);
         }
+      }
     }
     if (p.causal && tm.tmax > wp_lo) {
 #pragma unroll
