@@ -268,6 +268,11 @@ sage_kernel(const SageParams p) {
       float mx = -INFINITY;
       int kvh = kv - 32 * hh;        // keys of this lane half below the block size
       if (p.causal) kvh = min(kvh, p_row - bm[0].beta * 64 - 32 * hh + 1);
+      // sv * scl is the scaled score.  Blocks that no row of the wave cuts keep
+      // raw scores (scl = sc) and scale only their row max, |sc| times the max
+      // of sign(sc) * score, exact since scaling keeps or reverses the order;
+      // the scale then rides in the exponent's FMA.
+      float scl = 1.f;
       if (__builtin_amdgcn_ballot_w64(kvh < 32)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -278,15 +283,23 @@ sage_kernel(const SageParams p) {
             mx = fmaxf(mx, x);
           }
       } else {
-        // every key of the block is admitted in every row of the wave
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float x = (float)sacc[kb][i] * sc;
-            sv[kb][i] = x;
-            mx = fmaxf(mx, x);
-          }
+          for (int i = 0; i < 16; ++i) sv[kb][i] = (float)sacc[kb][i];
+        if (sc >= 0.f) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sv[kb][i]);
+        }
+        mx *= fabsf(sc);
+        scl = sc;
       }
       mx = half_max(mx);
       const float m_ref = (mx > m_run + kSlack) ? mx : m_run;
@@ -298,7 +311,7 @@ sage_kernel(const SageParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(sv[kb][i] - m_p8);
+          const float e = fast_exp2(__builtin_fmaf(sv[kb][i], scl, -m_p8));
           sv[kb][i] = e;
           psum += e;
         }
