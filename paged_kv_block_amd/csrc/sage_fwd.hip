@@ -200,6 +200,10 @@ sage_kernel(const SageParams p) {
   const int kswz = (ql >> 1) & 7;                    // rows 32kb + ql: same low bits
   const int vswz = (ql >> 2) & 3;                    // rows 32d + ql
 
+  // P^T operands (fp8 hi and lo parts): kept across blocks, so that each
+  // conversion's untouched half starts from the register it overwrites
+  // rather than from a fresh copy
+  i32x8 pb = {}, pl = {};
   for (int t = 0; t < n; ++t) {
     // block t landed in every wave's share; blocks t+1 .. t+kLA-1 may still fly
     int ahead = 0;
@@ -326,18 +330,17 @@ sage_kernel(const SageParams p) {
       l_run += psum;
       m_run = m_ref;
       // ---- P^T * kP8 -> fp8 as hi + lo parts, slot j = 16kb + i ----
-      i32x8 pb, pl;
 #pragma unroll
       for (int wd = 0; wd < 8; ++wd) {
         const int kb = wd >> 2;
         const int i0 = 4 * (wd & 3);
         const float x0 = sv[kb][i0], x1 = sv[kb][i0 + 1];
         const float x2 = sv[kb][i0 + 2], x3 = sv[kb][i0 + 3];
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, pb[wd], false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
         const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
         const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], 0, false);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], pl[wd], false);
         lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23[0], x3 - h23[1], lo, true);
         pb[wd] = hi;
         pl[wd] = lo;
