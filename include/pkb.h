@@ -320,8 +320,10 @@ int paged_decode_run(const void* query, const void* k, const void* v,
  * max_seq_len_q is the static bound).  Query i of request b sits at position
  * seq_len - qlen + i (bottom-right); causal needs qlen <= seq_len.
  *
- * Split policy and workspace: same chunk policy as paged_decode_workspace_size;
- * fp32 partials [B, max_q, Hq, num_splits, D+4] (max_q = seq_len_q, or
+ * Split policy and workspace: the chunk policy of paged_decode_workspace_size,
+ * except that with max_q > 1 the chunk length stops halving once the batch
+ * holds 4 (not 8) chunks per persistent wave (longer chunks: fewer partials to
+ * merge); fp32 partials [B, max_q, Hq, num_splits, D+4] (max_q = seq_len_q, or
  * max_seq_len_q when packed), written before they are read (no initialisation
  * needed). */
 int paged_decode_q_workspace_size(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t D,
