@@ -434,7 +434,9 @@ int qsa_validate(int32_t T, int32_t NB, const int32_t* lo_h, const int32_t* hi_h
  * block_first / block_last need not be passed: under the partition contract a
  * block's span follows from tok_base and blk_base, which the kernel uses.
  * D in {128, 256} (the page: 256), Hq / Hkv <= 16 (the page: 12), block_size
- * must be 4, scale finite (used as given; the page's default is 1/sqrt(256)).
+ * must be 4, scale finite (used as given; the page's default is 1/sqrt(256)),
+ * and each of k / v at most 4 GiB (T * Hkv * D * 2 bytes; else
+ * PKB_ERR_UNSUPPORTED).
  * Outputs (each may be NULL, not all): out [T, Hq, D] bf16, out_f32
  * [T, Hq, D], lse [Hq, T] natural log (the page's layout).  Empty rows give
  * zeros and -inf. */

@@ -424,6 +424,8 @@ int qsa_run(const void* q, const void* k, const void* v, const uint8_t* sel_bloc
   if (!isfinite(scale)) return PKB_ERR_ARG;
   if (!q || !k || !v || !sel_blocks || !lo || !hi || !blk_base || !tok_base) return PKB_ERR_ARG;
   if (!out && !out_f32 && !lse) return PKB_ERR_ARG;
+  // the kernel addresses K / V rows with 32-bit byte offsets
+  if ((int64_t)T * Hkv * D * 2 > 0xFFFFFFFFLL) return PKB_ERR_UNSUPPORTED;
   pkb::QsaParams p;
   memset(&p, 0, sizeof(p));
   p.q = (const uint16_t*)q;

@@ -168,7 +168,14 @@ qsa_kernel(const QsaParams p) {
   const uint16_t* vb = p.v + (int64_t)kvh * D;
   // first token of block id (any in-bounds token for id < 0)
   auto first_tok = [&](int id) -> int { return id >= 0 ? tb + 4 * (id - bb) : tb; };
-  auto clamp_tok = [&](int x) -> int64_t { return (int64_t)min(max(x, 0), p.T - 1); };
+  auto clamp_tok = [&](int x) -> int { return min(max(x, 0), p.T - 1); };
+  // K / V pools are at most 4 GiB (checked at launch), so a row's byte offset
+  // from the head's base fits 32 bits: the loads take the base from SGPRs and
+  // one 32-bit offset per lane
+  const uint32_t tok_bytes = (uint32_t)(tok_stride * 2);
+  auto ld_row = [&](const uint16_t* base, uint32_t off) -> u32x4 {
+    return *(const u32x4*)((const char*)base + off);
+  };
 
   // V piece lane + 64i of a group is key 2i + lane/32 (D = 256) or 4i + lane/16
   // (D = 128): block v_block(i) (the same for the whole wave), token v_off(i)
@@ -185,14 +192,14 @@ qsa_kernel(const QsaParams p) {
       const int f0 = first_tok(id[4 * u]), f1 = first_tok(id[4 * u + 1]);
       const int f2 = first_tok(id[4 * u + 2]), f3 = first_tok(id[4 * u + 3]);
       const int f = q4 == 0 ? f0 : (q4 == 1 ? f1 : (q4 == 2 ? f2 : f3));
-      const uint16_t* row = kb + clamp_tok(f + (qn & 3)) * tok_stride + 8 * g;
+      const uint32_t row = (uint32_t)clamp_tok(f + (qn & 3)) * tok_bytes + 16u * g;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) ka[u][s] = as_bf16x8(ld_global_16(row + 32 * s));
+      for (int s = 0; s < KS; ++s) ka[u][s] = as_bf16x8(ld_row(kb, row + 64u * s));
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int f = first_tok(id[v_block(i)]);
-      vr[i] = ld_global_16(vb + clamp_tok(f + v_off(i)) * tok_stride + 8 * (lane & (D / 8 - 1)));
+      vr[i] = ld_row(vb, (uint32_t)clamp_tok(f + v_off(i)) * tok_bytes + 16u * (lane & (D / 8 - 1)));
     }
   };
 

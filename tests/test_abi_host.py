@@ -432,6 +432,22 @@ def test_sage_run_static_errors():
 
 # ----------------------------------------------------------------------------- QSA
 
+def test_qsa_run_static_errors():
+    # Rejected before any device work: the dummy pointers are never dereferenced.
+    L = P.lib()
+    d = ctypes.c_void_p(256)
+
+    def run(T=64, NB=16, Hq=12, Hkv=1, D=256, scale=0.0625, bs=4, q=d):
+        return L.qsa_run(q, d, d, d, d, d, d, d, T, NB, Hq, Hkv, D, scale, bs, d, None, None, None)
+    assert run(q=None) == M.PKB_ERR_ARG
+    assert run(T=0) == M.PKB_ERR_ARG
+    assert run(bs=8) == M.PKB_ERR_UNSUPPORTED
+    assert run(Hq=24) == M.PKB_ERR_UNSUPPORTED          # 24 query heads per KV head
+    assert run(scale=float("inf")) == M.PKB_ERR_ARG
+    # K / V rows are addressed with 32-bit byte offsets: each pool at most 4 GiB
+    assert run(T=(1 << 23) + 1, Hkv=1, D=256) == M.PKB_ERR_UNSUPPORTED
+
+
 def test_qsa_validate_matches_spec():
     rng = np.random.default_rng(6)
     case = W.make_qsa(60, [9, 1, 14, 4, 7], Hq=2, Hkv=1, D=16, p_sel=0.3, empty_rows=2)
