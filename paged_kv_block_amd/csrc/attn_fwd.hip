@@ -389,25 +389,32 @@ attn_fwd_kernel(const AttnParams p) {
   // This wave's share of tile j's copies into its K and V ring slots.  Lane l of K (V)
   // instruction i writes LDS bytes i*1024 + 16l: row i*KPI + l/LPK, physical
   // piece l%LPK, so it fetches the logical piece stored there.
-  auto issue_tile = [&](const TM& tm, int j) {
-    const uint32_t kst = lds_base + (j % Lay::NSK) * Lay::TILE_B;
-    const uint32_t vst = lds_base + Lay::V_BASE + (j % Lay::NSV) * Lay::TILE_B;
-    // rows past the sequence end read their chunk's first row instead; the
-    // per-row test is needed only when one of this wave's chunks is partial
+  // rows past the sequence end read their chunk's first row instead; the
+  // per-row test is needed only when one of this wave's chunks is partial
+  auto tile_whole = [&](const TM& tm) -> bool {
     bool whole = true;
 #pragma unroll
     for (int lc = 0; lc < CPW; ++lc) whole = whole && (tm.tsrc[lc] + 8 <= L);
-    if (whole) {
+    return whole;
+  };
+  // instruction ii of the copies of a whole tile j (no row of it past L)
+  auto issue_whole = [&](const TM& tm, int j, int ii) {
+    const uint32_t kst = lds_base + (j % Lay::NSK) * Lay::TILE_B;
+    const uint32_t vst = lds_base + Lay::V_BASE + (j % Lay::NSV) * Lay::TILE_B;
+    const int i = wave * IPW + ii;
+    const int lc = (ii * Lay::KPI) >> 3;   // = chunk (i * KPI) / 8 - wave * CPW
+    const int key = i * Lay::KPI + lane / Lay::LPK;
+    const uint32_t row = (uint32_t)((key & 7) * D * 2);
+    const int pp = lane % Lay::LPK;
+    lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst + i * 1024);
+    lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst + i * 1024);
+  };
+  auto issue_tile = [&](const TM& tm, int j) {
+    const uint32_t kst = lds_base + (j % Lay::NSK) * Lay::TILE_B;
+    const uint32_t vst = lds_base + Lay::V_BASE + (j % Lay::NSV) * Lay::TILE_B;
+    if (tile_whole(tm)) {
 #pragma unroll
-      for (int ii = 0; ii < IPW; ++ii) {
-        const int i = wave * IPW + ii;
-        const int lc = (ii * Lay::KPI) >> 3;   // = chunk (i * KPI) / 8 - wave * CPW
-        const int key = i * Lay::KPI + lane / Lay::LPK;
-        const uint32_t row = (uint32_t)((key & 7) * D * 2);
-        const int pp = lane % Lay::LPK;
-        lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst + i * 1024);
-        lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst + i * 1024);
-      }
+      for (int ii = 0; ii < IPW; ++ii) issue_whole(tm, j, ii);
     } else {
 #pragma unroll
       for (int ii = 0; ii < IPW; ++ii) {
@@ -503,7 +510,9 @@ attn_fwd_kernel(const AttnParams p) {
   };
   // S^T for the tile whose K sits in ring slot `slot`
   // (K fragments are read kKPre k-steps ahead of their MFMAs.)
-  auto compute_s = [&](int slot, f32x16 (&acc)[2]) {
+  // When `cp` is set, the copies of whole tile cj go out one instruction per
+  // k-step, in the shadow of the MFMAs (the slot they fill is not read here).
+  auto compute_s = [&](int slot, f32x16 (&acc)[2], const TM* cp, int cj) {
     constexpr int kKPre = 4;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -525,6 +534,12 @@ attn_fwd_kernel(const AttnParams p) {
       if (s + kKPre < NKS) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) kr[s % kKPre][kb] = k_frag(slot, kb, s + kKPre);
+      }
+      if (cp) {
+        constexpr int per = (IPW + NKS - 1) / NKS;
+#pragma unroll
+        for (int u = 0; u < per; ++u)
+          if (s * per + u < IPW) issue_whole(*cp, cj, s * per + u);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -639,14 +654,18 @@ attn_fwd_kernel(const AttnParams p) {
     if (LA == 2 && j + 1 < n_tiles && tmr[1].M) wait_vmcnt<2 * IPW>();
     else wait_vmcnt<0>();
     __syncthreads();     // ... and is visible; every wave is done with tile j-1
-    if (tmr[LA].M) issue_tile(tmr[LA], j + LA);   // slots of tile j-1
-    if (wave_rows && tmr[0].M) {
+    // copies into the slots of tile j-1: a whole tile's go out during S
+    const bool run = wave_rows && tmr[0].M;
+    const bool in_s = run && tmr[LA].M && tile_whole(tmr[LA]);
+    if (tmr[LA].M && !in_s) issue_tile(tmr[LA], j + LA);
+    if (run) {
       // The SIMD's other wave belongs to another workgroup and is usually in a
       // different phase: raising this wave's priority while it issues MFMAs
       // keeps the matrix pipe fed while the other one runs its softmax.
       f32x16 sc[2];
       __builtin_amdgcn_s_setprio(1);
-      compute_s(j % Lay::NSK, sc);
+      if (in_s) compute_s(j % Lay::NSK, sc, &tmr[LA], j + LA);
+      else compute_s(j % Lay::NSK, sc, nullptr, 0);
       __builtin_amdgcn_s_setprio(0);
       mask_s(tmr[0], sc);
       softmax(sc);
