@@ -548,18 +548,21 @@ attn_fwd_kernel(const AttnParams p) {
   auto mask_s = [&](const TM& tm, f32x16 (&acc)[2]) {
     auto chunk_t = [&](int c) { return CONTIG ? tm.t0 + 8 * c : tm.ts[c]; };
     if (tm.M != ~0ull) {
-      // lanes 0-31 take key bit pos, lanes 32-63 bit pos + 4: a scalar lane
-      // mask whose halves are those bits sign-extended (one bit-field extract
-      // each)
+      // Only the 8-key chunks with an excluded key are touched (a few invalid
+      // keys leave most chunks whole).  Chunk c holds elements 4(c&3) .. +3 of
+      // block c>>2; lanes 0-31 take chunk bit r, lanes 32-63 bit r + 4: a
+      // scalar lane mask whose halves are those bits sign-extended.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t word = (uint32_t)(tm.M >> (32 * kb));
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t cb = (uint32_t)(tm.M >> (8 * c)) & 0xFFu;
+        if (cb != 0xFFu) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int pw = 8 * (i >> 2) + (i & 3);
-          const uint32_t lo = (uint32_t)((int32_t)(word << (31 - pw)) >> 31);
-          const uint32_t hi = (uint32_t)((int32_t)(word << (27 - pw)) >> 31);
-          acc[kb][i] = select_lanes((uint64_t)lo | ((uint64_t)hi << 32), acc[kb][i], neg_inf);
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t lo = (uint32_t)((int32_t)(cb << (31 - r)) >> 31);
+            const uint32_t hi = (uint32_t)((int32_t)(cb << (27 - r)) >> 31);
+            acc[c >> 2][4 * (c & 3) + r] =
+                select_lanes((uint64_t)lo | ((uint64_t)hi << 32), acc[c >> 2][4 * (c & 3) + r], neg_inf);
+          }
         }
       }
     }
