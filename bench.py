@@ -474,7 +474,7 @@ def main(argv=None):
                          "on until 0.2 s of untimed work has run)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["decode", "decode_q", "bsa", "prefill", "prefill256", "tiny",
+    ap.add_argument("--only", choices=["decode", "decode_q", "bsa", "prefill", "prefill_w1024", "prefill256", "tiny",
                                        "sage", "qsa", "copy"], default=None,
                     help="run one workload only (for profiling; copy = counter calibration)")
     a = ap.parse_args(argv)
@@ -492,6 +492,7 @@ def main(argv=None):
     if a.only and a.only != "decode":
         fn = {"bsa": lambda: bench_bsa_long(a.steps, a.warmup, W, P),
               "prefill": lambda: bench_prefill(a.steps, a.warmup, W, P),
+              "prefill_w1024": lambda: bench_prefill(a.steps, a.warmup, W, P, window_left=1024),
               "prefill256": lambda: bench_prefill(a.steps, a.warmup, W, P, D=256),
               "tiny": lambda: bench_bsa_tiny(a.steps, a.warmup, W, P),
               "sage": lambda: bench_sage(a.steps, a.warmup, W, P),
