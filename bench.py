@@ -3,8 +3,9 @@
 
 Headline (the single JSON line's ``value``): batch paged decode, KV-read GB/s --
 B=64 requests, Hq=32 / Hkv=8, D=128, seq_lens ~ U{512..8192}, 16-token pages
-with randomly permuted CSR page IDs, bf16.  One step = one decode launch over
-the whole batch (the split-KV kernel plus its small merge kernel).
+with randomly permuted CSR page IDs, bf16.  One step = one decode call over the
+whole batch (at this batch width a single kernel; narrower batches add a small
+merge kernel after the split-KV kernel).
 
 Secondary entries (same JSON line, ``secondary``): long-context block-sparse
 attention (B=4, S=8192, Hq=32/Hkv=8, 16 blocks of 64 per BSR row, causal, 1%
@@ -203,10 +204,11 @@ def bench_decode(steps, warmup, W, P):
            "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "page_size": ps,
            "sum_seq_len": int(case.seq_lens.sum()), "num_splits": S, "split_len": split_len,
            "kv_bytes_per_step": kv_bytes}
+    kern = ["decode_coop_kernel<128>"] if S == 1 else ["decode_kernel<128>", "decode_merge_kernel<128>"]
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(["decode_kernel<128>", "decode_merge_kernel<128>"], "decode"),
-            "kernel": "decode_kernel<128> + decode_merge_kernel<128> (one step)",
+            "traffic": measured_traffic(kern, "decode"),
+            "kernel": " + ".join(kern) + " (one step)",
             "per_unit": "4096 B of K+V per live token (Hkv=8, D=128, bf16)"}
     return case, gbs, ms_step, cfg, roof
 
@@ -233,6 +235,7 @@ def bench_decode_q(steps, warmup, W, P, SQ=4):
 
     ms_step, ms_launch = time_launches(step, steps, warmup)
     kv_bytes = int(case.seq_lens.astype(np.int64).sum()) * Hkv * D * 2 * 2
+    kern = ["decode_coop_kernel<128>"] if S == 1 else ["decode_kernel<128>", "decode_merge_kernel<128>"]
     return {"workload": f"multi-token paged decode B=64 SQ={SQ} Hq=32 Hkv=8 D=128 causal "
                         "seq_lens~U[512,8192] page_size=16 bf16 (seed 2)",
             "metric": "decode KV-read GB/s", "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
@@ -240,10 +243,9 @@ def bench_decode_q(steps, warmup, W, P, SQ=4):
             "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "achieved": round(kv_bytes / (ms_launch * 1e-3) / 1e9, 1),
                          "frac": round(kv_bytes / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(["decode_kernel<128>",
-                                                      "decode_merge_kernel<128>"], "decode_q"),
-                         "kernel": "decode_kernel<128> + decode_merge_kernel<128> (16 query "
-                                   "rows per KV head: 4 tokens x 4 heads)"}}
+                         "traffic": measured_traffic(kern, "decode_q"),
+                         "kernel": " + ".join(kern) + " (16 query rows per KV head: 4 tokens x "
+                                   "4 heads)"}}
 
 
 def bench_bsa_long(steps, warmup, W, P):

@@ -186,7 +186,8 @@ int bsa_validate(const bsa_plan_t* plan,
  *   kv_page_stride apart, one KV head kv_head_stride apart, tokens D apart);
  *   paged_kv_indptr/indices, block_indptr/indices, seq_lens_kv as in bsa_validate;
  *   kv_valid_bits [B, valid_words] uint32 or NULL (bit t%32 of word t/32, LSB
- *   first; 0 excludes token t);  sm_scale <= 0 selects 1/sqrt(D);
+ *   first; 0 excludes token t);  sm_scale: NaN selects 1/sqrt(D), any other
+ *   value must be finite and positive (else PKB_ERR_ARG);
  *   out [B, Sq, Hq, D] in plan->a.out_dtype;  lse [B*Sq, Hq] fp32 or NULL.
  * No workspace is needed. */
 int bsa_run(const bsa_plan_t* plan, const void* q, const void* k, const void* v,
@@ -264,8 +265,10 @@ int paged_prefill_plan_capacity(const prefill_static_args* args, int32_t max_qle
                                 pkb_prefill_plan_t* plan, int32_t* worklist_h,
                                 int64_t worklist_cap, int64_t* n_work);
 
-/* Trusted run.  worklist_d: device copy of the plan's work list.  output_scale
- * multiplies the normalised output; out dtype from the plan. */
+/* Trusted run.  worklist_d: device copy of the plan's work list.  sm_scale as
+ * for bsa_run (NaN selects 1/sqrt(D); otherwise finite and positive);
+ * output_scale (finite) multiplies the normalised output; out dtype from the
+ * plan. */
 int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
                       const void* q, const void* k_cache, const void* v_cache,
                       int64_t kv_page_stride, int64_t kv_head_stride,
@@ -300,7 +303,8 @@ int paged_decode_validate(int32_t B, int32_t num_pages, int32_t page_size,
                           const int32_t* seq_lens_h, pkb_bad_t* bad);
 
 /* Trusted run.  query [B, Hq, D] bf16; k/v pools as above; bmm1_scale is the
- * softmax scale (<= 0 selects 1/sqrt(D)); bmm2_scale multiplies the output;
+ * softmax scale (NaN selects 1/sqrt(D); any other value must be finite and
+ * positive, else PKB_ERR_ARG); bmm2_scale (finite) multiplies the output;
  * out [B, Hq, D] (out_dtype), lse [B, Hq] fp32 or NULL; workspace of at least
  * paged_decode_workspace_size() bytes, exclusive to this launch until it ends.
  * With more than one split a second, small kernel merges the partials. */
@@ -391,7 +395,8 @@ int bsa_sage_validate(const int32_t* q2k_block_index_h, int32_t capacity,
  *   the caller promises that each row's blocks are index[0], index[0] + 1, ...;
  *   only index[0] is read (Parameters: the promise is trusted, not checked).
  *   Block ids outside [0, ceil(Sk/64)) then count as empty blocks;
- *   softmax_scale <= 0 selects 1/sqrt(128);
+ *   softmax_scale: NaN selects 1/sqrt(128); otherwise it must be finite and
+ *   positive (the page asks for a positive scale), else PKB_ERR_ARG;
  *   mask_type: PKB_MASK_DENSE as on the page, or PKB_MASK_CAUSAL, an addition
  *   that applies the block-sparse page's token-level causal rule to the
  *   selected tokens (query i at position Sk - Sq + i admits tokens j <= that);

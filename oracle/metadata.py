@@ -293,11 +293,14 @@ def prefill_plan_capacity(args, max_qlen):
 # Decode
 # ----------------------------------------------------------------------------
 
-def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, per_wave=8):
-    """Chunk (split) policy from the static maximum length: chunk length CH
-    starts at 1024 tokens (doubled while a request would need > 4096 chunks),
-    then halves down to 64 until B*Hkv*ceil(max_seq_len/CH) >= per_wave items
-    per persistent wave (4 waves per CU).  Returns (status, bytes, chunks, CH)."""
+def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, per_wave=8, max_q=1):
+    """Chunk (split) policy from the static maximum length.  A wide batch -- at
+    most 16 query rows per KV head (max_q * Hq/Hkv), at most 256 requests and
+    B*Hkv >= 2*num_cus -- runs in one pass: one chunk of max_seq_len tokens, no
+    workspace.  Otherwise the chunk length CH starts at 1024 tokens (doubled
+    while a request would need > 4096 chunks), then halves down to 64 until
+    B*Hkv*ceil(max_seq_len/CH) >= per_wave items per persistent wave (4 waves
+    per CU).  Returns (status, bytes, chunks, CH)."""
     if min(B, Hq, Hkv, num_cus) < 1 or page_size < 1:
         return PKB_ERR_ARG, 0, 0, 0
     if Hq % Hkv:
@@ -306,6 +309,8 @@ def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, per_wave=8):
         return PKB_ERR_UNSUPPORTED, 0, 0, 0
     if not (1 <= max_seq_len <= MAX_SEQ_LEN):
         return PKB_ERR_ARG, 0, 0, 0
+    if max_q * (Hq // Hkv) <= 16 and B <= 256 and B * Hkv >= 2 * num_cus:
+        return PKB_OK, 0, 1, max_seq_len
     CH = 1024
     while cdiv(max_seq_len, CH) > 4096:
         CH *= 2
@@ -338,7 +343,7 @@ def decode_q_policy(B, max_q, Hq, Hkv, D, max_seq_len, page_size, num_cus):
     if max_q < 1:
         return PKB_ERR_ARG, 0, 0, 0
     st, nbytes, S, CH = decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus,
-                                      4 if max_q > 1 else 8)
+                                      4 if max_q > 1 else 8, max_q)
     if st != PKB_OK:
         return st, 0, 0, 0
     return PKB_OK, nbytes * max_q, S, CH

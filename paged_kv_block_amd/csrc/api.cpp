@@ -25,8 +25,16 @@ inline int hip_status(hipError_t e) {
   return PKB_ERR_HIP;
 }
 
-inline float scale_or_default(float s, int D) {
-  return (s > 0.f && isfinite(s)) ? s : 1.0f / sqrtf((float)D);
+// Softmax scale: NaN selects the default 1/sqrt(D); any other value must be
+// finite and positive.  Returns false for a scale the pages do not allow.
+inline bool resolve_scale(float s, int D, float* out) {
+  if (isnan(s)) {
+    *out = 1.0f / sqrtf((float)D);
+    return true;
+  }
+  if (!(s > 0.f) || !isfinite(s)) return false;
+  *out = s;
+  return true;
 }
 
 // Merge of split partials [B, maxq, Hq, S, D+4] into out / lse.
@@ -73,6 +81,8 @@ int bsa_run(const bsa_plan_t* plan, const void* q, const void* k, const void* v,
   if (kv_page_stride < (int64_t)a.Hkv * a.page_size * a.D ||
       kv_head_stride < (int64_t)a.page_size * a.D)
     return PKB_ERR_SHAPE;
+  float scale = 0.f;
+  if (!resolve_scale(sm_scale, a.D, &scale)) return PKB_ERR_ARG;
   AttnParams p;
   memset(&p, 0, sizeof(p));
   p.q = (const uint16_t*)q;
@@ -105,7 +115,7 @@ int bsa_run(const bsa_plan_t* plan, const void* q, const void* k, const void* v,
   p.num_splits = 1;
   p.split_len = 0;
   p.out_f32 = a.out_dtype == PKB_FP32;
-  p.scale_log2 = scale_or_default(sm_scale, a.D) * 1.4426950408889634f;
+  p.scale_log2 = scale * 1.4426950408889634f;
   p.out_scale = 1.0f;
   const int64_t total = (int64_t)plan->grid_x * plan->grid_y * plan->grid_z;
   dim3 grid((unsigned)(((total + 7) / 8) * 8), 1, 1);
@@ -135,6 +145,8 @@ int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
       kv_head_stride < (int64_t)a.page_size * a.D)
     return PKB_ERR_SHAPE;
   if (!isfinite(output_scale)) return PKB_ERR_ARG;
+  float scale = 0.f;
+  if (!resolve_scale(sm_scale, a.D, &scale)) return PKB_ERR_ARG;
   if (plan->n_work == 0) return PKB_OK;
   if (!worklist_d) return PKB_ERR_WORKSPACE;
   AttnParams p;
@@ -160,7 +172,7 @@ int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
   p.window_left = a.window_left;
   p.num_splits = 1;
   p.out_f32 = a.out_dtype == PKB_FP32;
-  p.scale_log2 = scale_or_default(sm_scale, a.D) * 1.4426950408889634f;
+  p.scale_log2 = scale * 1.4426950408889634f;
   p.out_scale = output_scale;
   dim3 grid(plan->grid_x * plan->grid_y, 1, 1);
   return hip_status(pkb::launch_attn(p, a.D, plan->waves, pkb::kModePrefill, grid,
@@ -192,7 +204,9 @@ int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv
   const hipStream_t s = (hipStream_t)stream;
   dim3 grid(S, Hkv, B);
   float* part = S > 1 ? (float*)workspace : nullptr;
-  const float sl2 = scale_or_default(bmm1_scale, D) * 1.4426950408889634f;
+  float scale = 0.f;
+  if (!resolve_scale(bmm1_scale, D, &scale)) return PKB_ERR_ARG;
+  const float sl2 = scale * 1.4426950408889634f;
   if (Hq / Hkv <= pkb::kDecodeMaxGroup) {
     pkb::DecodeParams d;
     memset(&d, 0, sizeof(d));
@@ -220,6 +234,8 @@ int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv
     d.out_f32 = out_dtype == PKB_FP32;
     d.scale_log2 = sl2;
     d.out_scale = bmm2_scale;
+    // wide batches: one pass, every (request, KV head) a whole item (S == 1)
+    if (pkb::decode_coop(B, Hkv, Hq / Hkv, num_cus)) return hip_status(pkb::launch_decode_coop(d, D, num_cus, s));
     const int64_t items = (int64_t)B * Hkv * S;
     const int waves = (int)std::min<int64_t>(items, (int64_t)num_cus * pkb::decode_waves_per_cu(D));
     hipError_t e = pkb::launch_decode(d, D, waves, s);
@@ -287,7 +303,9 @@ int paged_decode_q_run(const void* query, const void* k, const void* v, int64_t 
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKB_ERR_WORKSPACE;
   float* part = S > 1 ? (float*)workspace : nullptr;
   const hipStream_t s = (hipStream_t)stream;
-  const float sl2 = scale_or_default(bmm1_scale, D) * 1.4426950408889634f;
+  float scale = 0.f;
+  if (!resolve_scale(bmm1_scale, D, &scale)) return PKB_ERR_ARG;
+  const float sl2 = scale * 1.4426950408889634f;
   if ((int64_t)maxq * (Hq / Hkv) <= pkb::kDecodeMaxGroup) {
     // the query rows of a KV head fit the 16 MFMA columns of the decode kernel
     pkb::DecodeParams d;
@@ -318,6 +336,8 @@ int paged_decode_q_run(const void* query, const void* k, const void* v, int64_t 
     d.out_f32 = out_dtype == PKB_FP32;
     d.scale_log2 = sl2;
     d.out_scale = bmm2_scale;
+    if (pkb::decode_coop(B, Hkv, maxq * (Hq / Hkv), num_cus))
+      return hip_status(pkb::launch_decode_coop(d, D, num_cus, s));
     const int64_t items = (int64_t)B * Hkv * S;
     const int waves = (int)std::min<int64_t>(items, (int64_t)num_cus * pkb::decode_waves_per_cu(D));
     hipError_t e = pkb::launch_decode(d, D, waves, s);
@@ -377,7 +397,8 @@ int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
   if (block_sparse_num < 0 || block_sparse_num > capacity) return PKB_ERR_ARG;
   if (contiguous_block_indices && !uniform_block_count) return PKB_ERR_ARG;
   if (block_sizes && (block_sizes_rank < 1 || block_sizes_rank > 3)) return PKB_ERR_ARG;
-  if (!(softmax_scale <= 0.f) && !isfinite(softmax_scale)) return PKB_ERR_ARG;
+  float scale = 0.f;
+  if (!resolve_scale(softmax_scale, 128, &scale)) return PKB_ERR_ARG;
   if (!q_int8 || !k_int8 || !v_fp8 || !q_scale || !k_scale || !v_scale || !out)
     return PKB_ERR_ARG;
   if (capacity > 0 && !q2k_block_index) return PKB_ERR_ARG;
@@ -409,7 +430,7 @@ int bsa_sage_run(const void* q_int8, const void* k_int8, const void* v_fp8,
   p.block_sparse_num = block_sparse_num;
   p.bs_rank = block_sizes ? block_sizes_rank : 0;
   p.qs_len = (int)cdiv(Sq, 128) * 4;
-  p.scale_log2 = scale_or_default(softmax_scale, 128) * 1.4426950408889634f;
+  p.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(pkb::launch_sage(p, (hipStream_t)stream));
 }
 

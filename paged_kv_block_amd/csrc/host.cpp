@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "../../include/pkb.h"
+#include "policy.h"
 
 namespace {
 
@@ -310,18 +311,26 @@ int paged_prefill_plan_capacity(const prefill_static_args* a, int32_t max_qlen,
 
 // ------------------------------------------------------------------ decode
 
-// Chunk length CH (tokens per work item): start at 1024 (grown while a request
-// would need more than 4096 chunks), then halve down to 64 until the largest
-// possible item count reaches per_wave items per persistent wave (4 waves per
-// CU).  Multi-token decode aims at 4 items per wave: its merge reads max_q
-// times more partials, so fewer, longer chunks pay off there.
+// Single pass when the batch is wide enough (pkb::decode_coop): one chunk of
+// max_seq_len tokens per request, no workspace.  Otherwise the chunk length CH
+// (tokens per work item) starts at 1024 (grown while a request would need more
+// than 4096 chunks), then halves down to 64 until the largest possible item
+// count reaches per_wave items per persistent wave (4 waves per CU).
+// Multi-token decode aims at 4 items per wave: its merge reads max_q times more
+// partials, so fewer, longer chunks pay off there.
 static int decode_split(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len,
-                        int32_t page_size, int32_t num_cus, int per_wave, size_t* bytes,
-                        int32_t* num_splits, int32_t* split_len) {
+                        int32_t page_size, int32_t num_cus, int max_q, int per_wave,
+                        size_t* bytes, int32_t* num_splits, int32_t* split_len) {
   if (B < 1 || Hq < 1 || Hkv < 1 || num_cus < 1 || page_size < 1) return PKB_ERR_ARG;
   if (Hq % Hkv) return PKB_ERR_SHAPE;
   if ((D != 128 && D != 256) || page_size % 8) return PKB_ERR_UNSUPPORTED;
   if (max_seq_len < 1 || max_seq_len > PKB_MAX_SEQ_LEN) return PKB_ERR_ARG;
+  if (pkb::decode_coop(B, Hkv, (int)std::min<int64_t>((int64_t)max_q * (Hq / Hkv), 1 << 30), num_cus)) {
+    if (num_splits) *num_splits = 1;
+    if (split_len) *split_len = max_seq_len;
+    if (bytes) *bytes = 0;
+    return PKB_OK;
+  }
   int64_t CH = 1024;
   while (cdiv(max_seq_len, CH) > 4096) CH *= 2;
   const int64_t waves = 4LL * num_cus;
@@ -337,7 +346,7 @@ static int decode_split(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t m
 int paged_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                 int32_t max_seq_len, int32_t page_size, int32_t num_cus,
                                 size_t* bytes, int32_t* num_splits, int32_t* split_len) {
-  return decode_split(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, 8, bytes, num_splits,
+  return decode_split(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, 1, 8, bytes, num_splits,
                       split_len);
 }
 
@@ -360,8 +369,8 @@ int paged_decode_q_workspace_size(int32_t B, int32_t max_q, int32_t Hq, int32_t 
                                   size_t* bytes, int32_t* num_splits, int32_t* split_len) {
   if (max_q < 1) return PKB_ERR_ARG;
   size_t one = 0;
-  int st = decode_split(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, max_q > 1 ? 4 : 8, &one,
-                        num_splits, split_len);
+  int st = decode_split(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, max_q, max_q > 1 ? 4 : 8,
+                        &one, num_splits, split_len);
   if (st) return st;
   // fp32 partials [B, max_q, Hq, S, D+4]
   if (bytes) *bytes = one * (size_t)max_q;

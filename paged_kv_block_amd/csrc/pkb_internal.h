@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "policy.h"
+
 namespace pkb {
 
 enum AttnMode { kModeBsa = 0, kModePrefill = 1, kModeDecode = 2 };
@@ -40,12 +42,12 @@ struct AttnParams {
   float out_scale;
 };
 
-// Dedicated decode kernel (at most 16 query rows per KV head): a persistent
-// grid of single-wave workgroups, decode_waves_per_cu(D) per CU (one per
-// SIMD), each keeping one 32-key group of loads in flight while it computes
-// the previous one.
+// Dedicated decode kernels (at most kDecodeMaxGroup query rows per KV head).
+// The split kernel is a persistent grid of single-wave workgroups,
+// decode_waves_per_cu(D) per CU (one per SIMD), each keeping one 32-key group
+// of loads in flight while it computes the previous one; the cooperative
+// kernel runs kCoopWaves such waves per workgroup, one workgroup per CU.
 constexpr int decode_waves_per_cu(int) { return 4; }
-constexpr int kDecodeMaxGroup = 16;
 
 struct DecodeParams {
   const uint16_t* q;          // [tokens, Hq, D]
@@ -116,6 +118,7 @@ struct QsaParams {
 hipError_t launch_attn(const AttnParams& p, int D, int waves, int mode, dim3 grid,
                        hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int D, int grid, hipStream_t stream);
+hipError_t launch_decode_coop(const DecodeParams& p, int D, int grid, hipStream_t stream);
 hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream);
 hipError_t launch_sage(const SageParams& p, hipStream_t stream);
 hipError_t launch_qsa(const QsaParams& p, int D, hipStream_t stream);

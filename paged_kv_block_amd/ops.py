@@ -47,6 +47,20 @@ def _hp(a: Optional[np.ndarray]) -> Optional[int]:
     return None if a is None else a.ctypes.data
 
 
+def _scale(x) -> float:
+    """Softmax scale for the C ABI: None becomes NaN, the library's sentinel for
+    the default 1/sqrt(D); any given value is passed through unchanged (the
+    library rejects values that are not finite and positive)."""
+    return math.nan if x is None else float(x)
+
+
+def _mask(mask_type: str) -> int:
+    try:
+        return _MASK[mask_type]
+    except KeyError:
+        raise ValueError(f"mask_type must be 'dense' or 'causal', not {mask_type!r}") from None
+
+
 def _need(cond: bool, msg: str):
     if not cond:
         raise ValueError(msg)
@@ -111,7 +125,7 @@ def bsa_run(plan: BsaPlan, q, k_ptr, v_ptr, kv_page_stride, kv_head_stride, page
     st = lib().bsa_run(ctypes.byref(plan), _ptr(q), k_ptr, v_ptr, kv_page_stride, kv_head_stride,
                        _ptr(paged_kv_indptr), _ptr(paged_kv_indices), _ptr(block_indptr),
                        _ptr(block_indices), _ptr(seq_lens_kv), _ptr(kv_valid_bits),
-                       float(sm_scale or 0.0), _ptr(out), _ptr(lse),
+                       _scale(sm_scale), _ptr(out), _ptr(lse),
                        stream if stream is not None else _stream(q.device))
     check(st, "bsa_run")
 
@@ -126,8 +140,8 @@ class BlockSparsePagedWrapper:
                  device=None):
         self.plan = bsa_plan(B, Sq, Hq, Hkv, D, num_pages, page_size, q_block_size,
                              kv_block_size, max_seq_len_kv,
-                             C.PKB_MASK_CAUSAL if mask_type == "causal" else C.PKB_MASK_DENSE,
-                             window_left, C.PKB_BF16, _DTYPE[out_dtype], num_cus(device))
+                             _mask(mask_type), window_left, C.PKB_BF16, _DTYPE[out_dtype],
+                             num_cus(device))
         self.out_dtype = out_dtype
 
     def run(self, q, paged_kv_cache, paged_kv_indptr, paged_kv_indices, block_indptr,
@@ -190,8 +204,7 @@ def block_sparse_attention_with_paged_kv_cache(
 def _prefill_args(B, Hq, Hkv, D, num_pages, page_size, total_q, width, mask_type, window_left,
                   out_dtype, ncu):
     return PrefillStaticArgs(B, Hq, Hkv, D, num_pages, page_size, total_q, width,
-                             C.PKB_MASK_CAUSAL if mask_type == "causal" else C.PKB_MASK_DENSE,
-                             window_left, C.PKB_BF16, _DTYPE[out_dtype], ncu)
+                             _mask(mask_type), window_left, C.PKB_BF16, _DTYPE[out_dtype], ncu)
 
 
 def paged_prefill_validate(args: PrefillStaticArgs, qo_indptr, seq_lens_kv, block_tables,
@@ -242,7 +255,7 @@ def paged_prefill_run(plan: PrefillPlan, worklist_d, q, k_cache, v_cache, qo_ind
     st = lib().paged_prefill_run(ctypes.byref(plan), _ptr(worklist_d), _ptr(q), _ptr(k_cache),
                                  _ptr(v_cache), k_cache.stride(0), k_cache.stride(1),
                                  _ptr(qo_indptr), _ptr(block_tables), block_tables.stride(0),
-                                 _ptr(seq_lens_kv), float(sm_scale or 0.0), float(output_scale),
+                                 _ptr(seq_lens_kv), _scale(sm_scale), float(output_scale),
                                  _ptr(out), _ptr(lse),
                                  stream if stream is not None else _stream(q.device))
     check(st, "paged_prefill_run")
@@ -374,8 +387,8 @@ def paged_decode_run(query, kv_cache, paged_kv_indptr, paged_kv_indices, seq_len
     st = lib().paged_decode_run(_ptr(query), kp, vp, pst, hst, _ptr(paged_kv_indptr),
                                 _ptr(paged_kv_indices), _ptr(seq_lens), B, Hq, Hkv, D, P, ps,
                                 int(max_seq_len),
-                                C.PKB_MASK_CAUSAL if mask_type == "causal" else C.PKB_MASK_DENSE,
-                                int(window_left), float(bmm1_scale or 0.0), float(bmm2_scale),
+                                _mask(mask_type), int(window_left), _scale(bmm1_scale),
+                                float(bmm2_scale),
                                 _DTYPE[out.dtype], _ptr(out), _ptr(lse), ws_ptr, ws_bytes,
                                 num_cus_ if num_cus_ is not None else num_cus(query.device),
                                 stream if stream is not None else _stream(query.device))
@@ -424,7 +437,7 @@ def paged_decode_q_validate(B, num_pages, page_size, max_seq_len, paged_kv_indpt
     bad = Bad()
     st = lib().paged_decode_q_validate(B, num_pages, page_size, max_seq_len, _hp(ip), _hp(ix),
                                        ix.size, _hp(sl), _hp(qo), int(total_q), int(seq_len_q),
-                                       int(max_seq_len_q), _MASK[mask_type], ctypes.byref(bad))
+                                       int(max_seq_len_q), _mask(mask_type), ctypes.byref(bad))
     if raise_on_error:
         check(st, "paged_decode_q_validate", bad)
     return st, bad.field, bad.index
@@ -463,8 +476,8 @@ def paged_decode_q_run(query, kv_cache, paged_kv_indptr, paged_kv_indices, seq_l
     st = lib().paged_decode_q_run(_ptr(query), kp, vp, pst, hst, _ptr(paged_kv_indptr),
                                   _ptr(paged_kv_indices), _ptr(seq_lens), _ptr(qo_indptr), B,
                                   int(Sq), int(max_seq_len_q), Hq, Hkv, D, P, ps,
-                                  int(max_seq_len), _MASK[mask_type], int(window_left),
-                                  float(bmm1_scale or 0.0), float(bmm2_scale),
+                                  int(max_seq_len), _mask(mask_type), int(window_left),
+                                  _scale(bmm1_scale), float(bmm2_scale),
                                   _DTYPE[out.dtype], _ptr(out), _ptr(lse), ws_ptr, ws_bytes,
                                   num_cus_ if num_cus_ is not None else num_cus(query.device),
                                   stream if stream is not None else _stream(query.device))
@@ -516,7 +529,7 @@ def bsa_sage_run(q_int8, k_int8, v_fp8, q_scale, k_scale, v_scale, q2k_block_ind
                             _ptr(v_scale), _ptr(q2k_block_index), cap, int(block_sparse_num),
                             _ptr(block_sizes), rank, _ptr(q2k_block_nums),
                             int(bool(uniform_block_count)), int(bool(contiguous_block_indices)),
-                            B, H, Sq, Sk, float(softmax_scale or 0.0), _MASK[mask_type],
+                            B, H, Sq, Sk, _scale(softmax_scale), _mask(mask_type),
                             _ptr(out), _ptr(lse),
                             stream if stream is not None else _stream(q_int8.device))
     check(st, "bsa_sage_run")

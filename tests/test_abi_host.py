@@ -5,12 +5,14 @@ prefill work list and the decode split policy must match the Python statement
 of the same rules (oracle/metadata.py) bit for bit.
 """
 import ctypes
+import math
 import os
 import re
 import subprocess
 
 import numpy as np
 import pytest
+import torch
 
 import paged_kv_block_amd as P
 from paged_kv_block_amd import _lib as C
@@ -298,7 +300,20 @@ def test_decode_policy_matches_spec():
             continue
         got = P.paged_decode_workspace_size(B, Hq, Hkv, D, msl, ps, cus)
         assert got == (nbytes, S, sl)
-        assert S * sl >= msl and sl % 64 == 0
+        assert S * sl >= msl and (sl % 64 == 0 or (S == 1 and sl == msl and nbytes == 0))
+
+
+def test_decode_policy_single_pass_cases():
+    """Wide batches run in one pass (no workspace); the batch-decode workload
+    (B=64, Hq=32, Hkv=8 on 256 CUs) is one, and so is its 4-token variant.
+    Narrow batches, more than 256 requests or more than 16 query rows per KV
+    head keep the chunked policy."""
+    assert M.decode_policy(64, 32, 8, 128, 8192, 16, 256) == (0, 0, 1, 8192)
+    assert P.paged_decode_workspace_size(64, 32, 8, 128, 8192, 16, 256) == (0, 1, 8192)
+    assert M.decode_q_policy(64, 4, 32, 8, 128, 8192, 16, 256) == (0, 0, 1, 8192)
+    assert M.decode_policy(63, 32, 8, 128, 8192, 16, 256)[2] > 1      # 504 < 512 items
+    assert M.decode_policy(257, 32, 8, 128, 8192, 16, 256)[2] > 1     # too many to order in LDS
+    assert M.decode_q_policy(64, 5, 32, 8, 128, 8192, 16, 256)[2] > 1  # 20 query rows per KV head
 
 
 def test_decode_validate_matches_spec():
@@ -420,12 +435,15 @@ def test_sage_run_static_errors():
     L = P.lib()
     d = ctypes.c_void_p(256)
 
-    def run(B=1, H=1, Sq=64, Sk=64, q=d, mask=M.DENSE):
+    def run(B=1, H=1, Sq=64, Sk=64, q=d, mask=M.DENSE, scale=math.nan):
         return L.bsa_sage_run(q, d, d, d, d, d, d, 1, 1, None, 0, None, 0, 0,
-                              B, H, Sq, Sk, 0.0, mask, d, None, None)
+                              B, H, Sq, Sk, scale, mask, d, None, None)
     assert run(q=None) == M.PKB_ERR_ARG
     assert run(Sk=0) == M.PKB_ERR_ARG
     assert run(mask=7) == M.PKB_ERR_ARG
+    # the page asks for a positive scale; NaN is the default's sentinel
+    for bad in (0.0, -0.5, math.inf, -math.inf):
+        assert run(scale=bad) == M.PKB_ERR_ARG, bad
     # V^T offsets inside one head are 32-bit: Sk up to 2^25
     assert run(Sk=(1 << 25) + 1) == M.PKB_ERR_UNSUPPORTED
 
@@ -473,3 +491,37 @@ def test_qsa_validate_matches_spec():
         n_bad += want[0] != 0
     assert n_bad > 150
     assert M.qsa_validate(*base) == M.OK
+
+
+# ----------------------------------------------------------------------------- scales
+
+def test_runs_reject_bad_softmax_scales():
+    """A softmax scale that is zero, negative or not finite is rejected before
+    anything is launched (NaN alone selects the default 1/sqrt(D)); the dummy
+    device pointers are never dereferenced.  Only rejections are exercised
+    here: an accepted scale would launch a kernel."""
+    L = P.lib()
+    d = ctypes.c_void_p(256)
+    bsa = P.bsa_plan(1, 64, 4, 1, 128, 8, 16, 16, 64, 128, M.CAUSAL, num_cus_=256)
+    pre_args = P.ops._prefill_args(1, 4, 1, 128, 8, 16, 64, 8, "causal", -1, torch.bfloat16, 256)
+    pre, _ = P.paged_prefill_plan(pre_args, [0, 64], [100])
+    for bad in (0.0, -1.0, math.inf, -math.inf):
+        assert L.bsa_run(ctypes.byref(bsa), d, d, d, 8 * 16 * 128, 16 * 128, d, d, d, d, d, None,
+                         bad, d, None, None) == M.PKB_ERR_ARG, bad
+        assert L.paged_prefill_run(ctypes.byref(pre), d, d, d, d, 16 * 128, 16 * 128, d, d, 8, d,
+                                   bad, 1.0, d, None, None) == M.PKB_ERR_ARG, bad
+        assert L.paged_decode_run(d, d, d, 8 * 16 * 128, 16 * 128, d, d, d, 4, 32, 8, 128, 64, 16,
+                                  512, M.DENSE, -1, bad, 1.0, 0, d, None, d, 1 << 30, 256,
+                                  None) == M.PKB_ERR_ARG, bad
+        assert L.paged_decode_q_run(d, d, d, 8 * 16 * 128, 16 * 128, d, d, d, None, 4, 2, 0, 32, 8,
+                                    128, 64, 16, 512, M.CAUSAL, -1, bad, 1.0, 0, d, None, d,
+                                    1 << 30, 256, None) == M.PKB_ERR_ARG, bad
+
+
+def test_binding_rejects_unknown_mask_strings():
+    """Mask names are looked up strictly: a misspelt name is an error, never a
+    silent dense mask."""
+    with pytest.raises(ValueError):
+        P.BlockSparsePagedWrapper(1, 64, 4, 1, 128, 8, 16, 16, 64, 128, "Causal")
+    with pytest.raises(ValueError):
+        P.ops._prefill_args(1, 4, 1, 128, 8, 16, 64, 8, "causal ", -1, torch.bfloat16, 256)

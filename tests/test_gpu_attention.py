@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_block_amd as P
 from gen import workloads as W
 from tests.gpu_util import (TOL_BF16, TOL_F32, TOL_LSE, assert_close, f64, oracle_bsa,
                             oracle_decode, oracle_decode_q, oracle_prefill, run_bsa, run_decode,
@@ -248,6 +249,59 @@ def test_decode_sweep(i):
     assert torch.equal(out_c, out) and torch.equal(lse_c, lse)
 
 
+# Wide batches run the single-pass kernel (whole (request, KV head) items
+# split over the waves of a workgroup, merged in LDS).  A small num_cus makes
+# small batches wide: several rounds of the snake deal per workgroup.
+COOP_SWEEP = [
+    # B, Hq, Hkv, D, seq_lens, ps, mask, w, num_cus
+    (6, 32, 8, 128, [1, 31, 32, 33, 127, 1000], 16, "dense", -1, 4),
+    (5, 16, 2, 256, [4097, 5, 300, 2049, 64], 32, "causal", 100, 3),
+    (7, 4, 1, 128, [129, 1, 2000, 64, 65, 700, 3], 8, "causal", 0, 2),
+    (4, 16, 1, 128, [333, 1024, 8, 5000], 16, "dense", -1, 2),       # G = 16
+    (9, 8, 8, 128, [100] * 9, 16, "dense", -1, 4),                    # MHA, equal lengths
+    (3, 32, 8, 256, [2, 130, 4096], 16, "causal", 1000, 12),
+]
+
+
+@pytest.mark.parametrize("i", range(len(COOP_SWEEP)))
+def test_decode_single_pass_sweep(i):
+    B, Hq, Hkv, D, sl, ps, mask, w, ncu = COOP_SWEEP[i]
+    _say("decode single-pass sweep", COOP_SWEEP[i])
+    assert P.paged_decode_workspace_size(B, Hq, Hkv, D, max(sl), ps, ncu)[:2] == (0, 1)
+    case = W.make_decode(530 + i, B, Hq, Hkv, D, sl, ps, mask=mask, window_left=w, extra_pages=2,
+                         bmm2_scale=0.8)
+    out, lse, S = run_decode(case, num_cus=ncu)
+    assert S == 1
+    ref_o, ref_l = oracle_decode(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, lse32, _ = run_decode(case, out_dtype=torch.float32, num_cus=ncu)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
+    assert_close(f64(lse32), ref_l, TOL_LSE, "lse (fp32 run)")
+    out_c, lse_c, _ = run_decode(case, combined=True, num_cus=ncu)
+    assert torch.equal(out_c, out) and torch.equal(lse_c, lse)
+
+
+def test_decode_single_pass_growing_scores():
+    """Key magnitudes grow along each request, so the waves that share an item
+    end with very different running maxima; their LDS merge must weight them
+    by those maxima."""
+    case = W.make_decode(561, 3, 16, 4, 128, [3000, 700, 1500], 16, extra_pages=2)
+    ps = case.k.shape[2]
+    k = case.k.float()
+    for b, L in enumerate(case.seq_lens):
+        pages = case.kv_indices[case.kv_indptr[b]:case.kv_indptr[b + 1]]
+        for t in range(int(L)):
+            k[int(pages[t // ps]), :, t % ps, :] *= 1.0 + t / 100.0
+    case.k = k.to(torch.bfloat16)
+    _say("decode single-pass growing scores")
+    out, lse, S = run_decode(case, num_cus=2)
+    assert S == 1
+    ref_o, ref_l = oracle_decode(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+
+
 def test_batch_decode_sampled():
     case = W.batch_decode()
     _say("batch_decode: generated", int(case.seq_lens.sum()))
@@ -276,6 +330,31 @@ DECODE_Q_SWEEP = [
     (2, 32, 8, 256, [333, 4097], 32, 2, "dense", -1, 256),
     (3, 8, 2, 128, [40, 64, 50], 16, 4, "causal", -1, 256),            # one split
 ]
+
+
+# single-pass kernel (tokens x group <= 16 and a wide batch for the given num_cus)
+DECODE_Q_COOP_SWEEP = [
+    (4, 32, 8, 128, [9, 3000, 4, 700], 16, [1, 4, 2, 3], "causal", 40, 8),
+    (5, 16, 4, 256, [16, 2049, 90, 5, 64], 16, 4, "causal", -1, 4),
+    (3, 4, 4, 128, [16, 1500, 40], 16, [16, 9, 1], "causal", 5, 2),     # MHA, qlen == L
+    (4, 8, 2, 128, [77, 1, 300, 4100], 16, 1, "dense", -1, 3),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DECODE_Q_COOP_SWEEP)))
+def test_decode_q_single_pass_sweep(i):
+    B, Hq, Hkv, D, sl, ps, sq, mask, w, ncu = DECODE_Q_COOP_SWEEP[i]
+    _say("decode_q single-pass sweep", DECODE_Q_COOP_SWEEP[i])
+    fixed = isinstance(sq, int)
+    case = W.make_decode_q(740 + i, B, Hq, Hkv, D, sl, ps, seq_len_q=sq if fixed else None,
+                           qlens=None if fixed else sq, mask=mask, window_left=w, extra_pages=2)
+    out, lse, S = run_decode_q(case, num_cus=ncu)
+    assert S == 1
+    ref_o, ref_l = oracle_decode_q(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, _, _ = run_decode_q(case, out_dtype=torch.float32, num_cus=ncu)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
 
 
 @pytest.mark.parametrize("i", range(len(DECODE_Q_SWEEP)))
