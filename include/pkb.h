@@ -318,6 +318,28 @@ int paged_decode_run(const void* query, const void* k, const void* v,
                      void* workspace, size_t workspace_bytes, int32_t num_cus,
                      void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as paged_decode_run, with the split partials in a fixed scratch
+ * array of PKB_DECODE_SCRATCH_BYTES (32 MiB) that the library holds on each
+ * device it runs on until the process ends.  Nothing is allocated per call.
+ * A call whose partials (paged_decode_workspace_size) exceed that size
+ * returns PKB_ERR_WORKSPACE before anything is enqueued.  Every call on one
+ * device shares that device's array: calls that overlap on one GPU (other
+ * streams, or a second call before the first has finished on the device)
+ * race and give undefined results.  The array needs no initialisation (every
+ * partial is written before it is read).  Other arguments and errors as
+ * paged_decode_run. */
+#define PKB_DECODE_SCRATCH_BYTES (32u << 20)
+int paged_decode_run_noalloc(const void* query, const void* k, const void* v,
+                             int64_t kv_page_stride, int64_t kv_head_stride,
+                             const int32_t* paged_kv_indptr, const int32_t* paged_kv_indices,
+                             const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                             int32_t D, int32_t num_pages, int32_t page_size,
+                             int32_t max_seq_len, int32_t mask_type, int32_t window_left,
+                             float bmm1_scale, float bmm2_scale, int32_t out_dtype, void* out,
+                             float* lse, int32_t num_cus, void* stream);
+
 /* Multi-token decode (decode page, description: for seq_len_q > 1 query and
  * output are token-major [B, SQ, Hq, D]; with qo_indptr they are packed
  * [total_q, Hq, D] and request b owns rows qo_indptr[b]:qo_indptr[b+1];

@@ -26,6 +26,7 @@ from .ops import (  # noqa: E402
     paged_decode_q_validate,
     paged_decode_q_workspace_size,
     paged_decode_run,
+    paged_decode_run_noalloc,
     paged_decode_validate,
     paged_decode_workspace_size,
     paged_prefill_plan,
@@ -44,7 +45,7 @@ __all__ = [
     "block_sparse_attention_with_paged_kv_cache", "bsa_attn_blk64_sage_fwd", "bsa_plan",
     "bsa_run", "bsa_sage_run", "bsa_sage_validate", "bsa_validate", "num_cus",
     "paged_decode_q_run", "paged_decode_q_validate", "paged_decode_q_workspace_size",
-    "paged_decode_run", "paged_decode_validate", "paged_decode_workspace_size",
+    "paged_decode_run", "paged_decode_run_noalloc", "paged_decode_validate", "paged_decode_workspace_size",
     "paged_prefill_plan", "paged_prefill_plan_capacity", "paged_prefill_run",
     "paged_prefill_validate", "qsa_forward", "qsa_run", "qsa_validate", "split_kv_cache",
 ]

@@ -24,6 +24,7 @@ PKB_ERR_HIP = -7
 PKB_BF16, PKB_FP32, PKB_I8, PKB_FP8E4M3 = 0, 1, 2, 3
 PKB_MASK_DENSE, PKB_MASK_CAUSAL = 0, 1
 PKB_MAX_SEQ_LEN = 2147483520
+PKB_DECODE_SCRATCH_BYTES = 32 << 20
 
 FIELD_NAMES = {0: "none", 1: "paged_kv_indptr", 2: "paged_kv_indices", 3: "seq_lens",
                4: "block_indptr", 5: "block_indices", 6: "qo_indptr", 7: "block_tables",
@@ -91,6 +92,11 @@ _SIGS = {
                                  c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_float, c_float, c_int32,
                                  c_void_p, c_void_p, c_void_p, c_size_t, c_int32, c_void_p]),
+    "paged_decode_run_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64,
+                                         c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                         c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                         c_float, c_float, c_int32, c_void_p, c_void_p, c_int32,
+                                         c_void_p]),
     "paged_decode_q_workspace_size": (c_int, [c_int32, c_int32, c_int32, c_int32, c_int32,
                                               c_int32, c_int32, c_int32, POINTER(c_size_t),
                                               POINTER(c_int32), POINTER(c_int32)]),

@@ -277,6 +277,31 @@ int paged_decode_run(const void* query, const void* k, const void* v, int64_t kv
   return PKB_OK;
 }
 
+int paged_decode_run_noalloc(const void* query, const void* k, const void* v,
+                             int64_t kv_page_stride, int64_t kv_head_stride,
+                             const int32_t* kv_indptr, const int32_t* kv_indices,
+                             const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                             int32_t num_pages, int32_t page_size, int32_t max_seq_len,
+                             int32_t mask_type, int32_t window_left, float bmm1_scale,
+                             float bmm2_scale, int32_t out_dtype, void* out, float* lse,
+                             int32_t num_cus, void* stream) {
+  size_t need = 0;
+  int32_t S = 0, split_len = 0;
+  int st = paged_decode_workspace_size(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, &need,
+                                       &S, &split_len);
+  if (st) return st;
+  if (need > pkb::kDecodeScratchBytes) return PKB_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = pkb::decode_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return paged_decode_run(query, k, v, kv_page_stride, kv_head_stride, kv_indptr, kv_indices,
+                          seq_lens, B, Hq, Hkv, D, num_pages, page_size, max_seq_len, mask_type,
+                          window_left, bmm1_scale, bmm2_scale, out_dtype, out, lse, ws, need,
+                          num_cus, stream);
+}
+
 int paged_decode_q_run(const void* query, const void* k, const void* v, int64_t kv_page_stride,
                        int64_t kv_head_stride, const int32_t* kv_indptr,
                        const int32_t* kv_indices, const int32_t* seq_lens,

@@ -33,6 +33,7 @@
 // fence, makes the partials visible: on this part such a fence writes back and
 // invalidates the whole L2 of an XCD.
 #include <atomic>
+#include <mutex>
 
 #include "device_common.h"
 #include "pkb_internal.h"
@@ -693,6 +694,36 @@ hipError_t launch_decode_coop(const DecodeParams& p, int D, int grid, hipStream_
   if (D == 128) return launch_coop<128>(p, grid, stream);
   if (D == 256) return launch_coop<256>(p, grid, stream);
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- fixed scratch
+// Split partials for callers that cannot allocate device memory: one
+// file-scope array per device, kDecodeScratchBytes large, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it only stands for the symbol); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in decode_scratch_ptr[].
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+static std::mutex decode_scratch_mu;
+static void* decode_scratch_ptr[kMaxDevices];
+
+hipError_t decode_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(decode_scratch_mu);
+  if (!decode_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    decode_scratch_ptr[dev] = p;
+  }
+  *ptr = decode_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream) {

@@ -120,6 +120,12 @@ hipError_t launch_attn(const AttnParams& p, int D, int waves, int mode, dim3 gri
 hipError_t launch_decode(const DecodeParams& p, int D, int grid, hipStream_t stream);
 hipError_t launch_decode_coop(const DecodeParams& p, int D, int grid, hipStream_t stream);
 hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream);
+
+// Fixed per-device scratch for the split partials of paged_decode_run_noalloc:
+// its device address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_sage(const SageParams& p, hipStream_t stream);
 hipError_t launch_qsa(const QsaParams& p, int D, hipStream_t stream);
 

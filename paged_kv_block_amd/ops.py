@@ -396,6 +396,35 @@ def paged_decode_run(query, kv_cache, paged_kv_indptr, paged_kv_indices, seq_len
     return out
 
 
+def paged_decode_run_noalloc(query, kv_cache, paged_kv_indptr, paged_kv_indices, seq_lens,
+                             max_seq_len, *, mask_type="dense", window_left=-1, bmm1_scale=None,
+                             bmm2_scale=1.0, out=None, lse=None, num_cus_=None, stream=None):
+    """paged_decode_run without a caller workspace: split partials go to the
+    library's fixed per-device scratch (PKB_DECODE_SCRATCH_BYTES).  Calls that
+    overlap on one GPU race on that scratch."""
+    kp, vp, pst, hst, P, Hkv, ps, D, dt, dev = split_kv_cache(kv_cache)
+    B, Hq, Dq = query.shape
+    _need(Dq == D and dt == torch.bfloat16 and query.dtype == torch.bfloat16 and query.is_contiguous(),
+          "query must be contiguous bf16 [B, Hq, D] matching the cache")
+    for t, n in ((paged_kv_indptr, "paged_kv_indptr"), (paged_kv_indices, "paged_kv_indices"),
+                 (seq_lens, "seq_lens")):
+        _dev_i32(t, n)
+    _need(out is not None and out.is_contiguous() and out.shape == query.shape
+          and out.dtype in _DTYPE, "out must be a contiguous [B, Hq, D] bf16 or fp32 tensor")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and lse.numel() == B * Hq and lse.is_contiguous(),
+              "lse must be fp32 [B, Hq]")
+    st = lib().paged_decode_run_noalloc(_ptr(query), kp, vp, pst, hst, _ptr(paged_kv_indptr),
+                                        _ptr(paged_kv_indices), _ptr(seq_lens), B, Hq, Hkv, D, P,
+                                        ps, int(max_seq_len), _mask(mask_type), int(window_left),
+                                        _scale(bmm1_scale), float(bmm2_scale), _DTYPE[out.dtype],
+                                        _ptr(out), _ptr(lse),
+                                        num_cus_ if num_cus_ is not None else num_cus(query.device),
+                                        stream if stream is not None else _stream(query.device))
+    check(st, "paged_decode_run_noalloc")
+    return out
+
+
 def batch_decode_with_paged_kv_cache(query, kv_cache, workspace_buffer, paged_kv_indptr,
                                      paged_kv_indices, seq_lens, max_seq_len, *, bmm1_scale=None,
                                      bmm2_scale=1.0, out=None, out_dtype=None, mask_type="dense",

@@ -525,3 +525,16 @@ def test_binding_rejects_unknown_mask_strings():
         P.BlockSparsePagedWrapper(1, 64, 4, 1, 128, 8, 16, 16, 64, 128, "Causal")
     with pytest.raises(ValueError):
         P.ops._prefill_args(1, 4, 1, 128, 8, 16, 64, 8, "causal ", -1, torch.bfloat16, 256)
+
+
+def test_noalloc_decode_rejects_oversized_partials_before_launch():
+    """The allocation-free decode checks its partials against the fixed scratch
+    (PKB_DECODE_SCRATCH_BYTES) before any device work; the dummy pointers are
+    never dereferenced."""
+    nbytes, S, _ = P.paged_decode_workspace_size(300, 32, 8, 256, 8192, 16, 256)
+    assert S > 1 and nbytes > C.PKB_DECODE_SCRATCH_BYTES == 32 << 20
+    d = ctypes.c_void_p(256)
+    st = P.lib().paged_decode_run_noalloc(d, d, d, 8 * 16 * 256, 16 * 256, d, d, d, 300, 32, 8,
+                                          256, 1000, 16, 8192, M.DENSE, -1, math.nan, 1.0, 0, d,
+                                          None, 256, None)
+    assert st == C.PKB_ERR_WORKSPACE
