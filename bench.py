@@ -10,20 +10,28 @@ merge kernel after the split-KV kernel).
 Secondary entries (same JSON line, ``secondary``): long-context block-sparse
 attention (B=4, S=8192, Hq=32/Hkv=8, 16 blocks of 64 per BSR row, causal, 1%
 invalid bits), packed causal prefill (B=8, qlen ~ U{256..2048} + prefix
-~ U{0..2048}), the Sage-style int8/fp8 block-sparse case (B=2, H=16, S=16384,
-64 of 256 blocks per query block) and the tiny block-sparse case -- each as
-TFLOP/s (TOP/s) over the admitted (query, key) pairs only (4*D operations per
-admitted pair and query head).
+~ U{0..2048}; D=128, window 1024, D=256), the Sage-style int8/fp8 block-sparse
+case (B=2, H=16, S=16384, 64 of 256 blocks per query block), multi-token
+decode, packed-query token-granular sparse attention and the tiny block-sparse
+case -- attention as TFLOP/s (TOP/s) over the admitted (query, key) pairs only
+(4*D operations per pair and query head).
 
-Timing: inputs are generated (seeded), copied to HBM and planned before the
-timed region; W warm-up launches, then K launches bracketed by device
-synchronisation, each launch also bracketed by HIP events on the stream it is
-enqueued on (torch's current stream).  ``cpu_baseline`` times the fp64 oracle
-on a bounded sample of the headline workload on the host cores.
+Timing: inputs are generated (seeded; their SHA-256 is reported), copied to
+HBM and planned before the timed region; W warm-up launches (and on until
+0.2 s of untimed work has run), then K launches between two HIP events (the
+step time), then K launches each bracketed by its own events on the stream
+they are enqueued on (the mean launch duration, ``roofline.achieved``).
+
+Roofline denominators: MI355X's published peaks, and the ceilings measured on
+the same device by libpkb_peaks.so (``peaks``; ``frac_measured``).
+``cpu_baseline`` times the fp64 oracle on bounded samples of the decode and
+long block-sparse workloads, in worker processes over every host core.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import math
 import os
@@ -34,11 +42,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import numpy as np  # noqa: E402
-import torch  # noqa: E402
+
+# The CPU-baseline workers are spawned processes that re-import this file as
+# "__mp_main__": they run NumPy only and never load torch (or its HIP runtime).
+if __name__ != "__mp_main__":
+    import torch  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 INT8_PEAK_TOPS = 5000.0        # dense int8 / fp8 MFMA
+
+PEAKS = {}                     # ceilings measured on this device (measure_peaks)
 
 
 def log(*a):
@@ -51,7 +65,6 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def _sha256(paths):
-    import hashlib
     h = hashlib.sha256()
     for path in paths:
         with open(path, "rb") as f:
@@ -82,6 +95,19 @@ def measured_traffic(kernels, workload):
             return None
         total += int(r["bytes_per_launch"])
     return total
+
+
+def input_sha256(*xs):
+    """SHA-256 over the bytes of the generated inputs (CPU tensors / arrays), in
+    argument order: identifies the exact synthetic draw a figure was taken on."""
+    h = hashlib.sha256()
+    for x in xs:
+        if x is None:
+            continue
+        if isinstance(x, torch.Tensor):
+            x = x.detach().contiguous().view(torch.uint8).numpy()
+        h.update(np.ascontiguousarray(x).view(np.uint8).data)
+    return h.hexdigest()
 
 
 def dev_i32(a):
@@ -125,10 +151,101 @@ def time_launches(fn, steps, warmup):
     return t0.elapsed_time(t1) / steps, float(np.mean(per))
 
 
+def roofline(bound, achieved, unit, peak, measured_key, traffic, kernel, **extra):
+    """Roofline entry: the published peak, and the ceiling measured on this
+    device (``PEAKS[measured_key]``) when the peaks were taken."""
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4) if peak else None, "traffic": traffic}
+    pm = PEAKS.get(measured_key) if measured_key else None
+    if pm:
+        r["peak_measured"] = round(pm, 1)
+        r["frac_measured"] = round(achieved / pm, 4)
+    r["kernel"] = kernel
+    r.update(extra)
+    return r
+
+
+# ---------------------------------------------------------------------------- on-device peaks
+
+def _peaks_lib():
+    path = os.path.join(ROOT, "paged_kv_block_amd", "libpkb_peaks.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with paged_kv_block_amd/build.py")
+    L = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.pkb_peak_hbm_read.argtypes = [vp, i64, vp, i32, vp]
+    L.pkb_peak_hbm_gather.argtypes = [vp, i64, i64, vp, i32, ctypes.POINTER(i64), vp]
+    L.pkb_peak_l2_gather.argtypes = [vp, i64, i64, vp, i32, ctypes.POINTER(i64), vp]
+    L.pkb_peak_mfma.argtypes = [i32, i32, vp, i32, vp]
+    for f in (L.pkb_peak_hbm_read, L.pkb_peak_hbm_gather, L.pkb_peak_l2_gather, L.pkb_peak_mfma):
+        f.restype = ctypes.c_int
+    return L
+
+
+def _best_ms(fn, n=10):
+    """Shortest of n launches, each between its own events, after >= 0.2 s of
+    untimed launches (clock ramp)."""
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < WARMUP_MIN_S:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return min(a.elapsed_time(b) for a, b in evs)
+
+
+def measure_peaks(P):
+    """Ceilings of this device from hand-written probe kernels: an HBM streaming
+    read of 4 GiB, a gather of random 4 KiB slabs (decode's access shape), a
+    gather of random 512-byte rows from a 2 MiB L2-resident buffer (the
+    packed-query kernel's), and dense MFMA loops at two waves per SIMD."""
+    L = _peaks_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    ncu = P.num_cus()
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out = {}
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed (HIP error {-rc})")
+
+    ms = _best_ms(lambda: ok(L.pkb_peak_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), ncu * 8, st),
+                             "hbm read"))
+    out["hbm_read_GBps"] = nbytes / (ms * 1e-3) / 1e9
+    got = ctypes.c_int64(0)
+    ms = _best_ms(lambda: ok(L.pkb_peak_hbm_gather(buf.data_ptr(), nbytes, 1 << 20, sink.data_ptr(),
+                                                   ncu * 4, ctypes.byref(got), st), "hbm gather"))
+    out["hbm_gather_4k_GBps"] = got.value / (ms * 1e-3) / 1e9
+    small = 2 << 20
+    ms = _best_ms(lambda: ok(L.pkb_peak_l2_gather(buf.data_ptr(), small, 1 << 24, sink.data_ptr(),
+                                                  ncu * 4, ctypes.byref(got), st), "l2 gather"))
+    out["l2_gather_512_GBps"] = got.value / (ms * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    grid, iters = ncu * 2, 4096
+    for kind, key, per in ((0, "mfma_bf16_TFLOPs", 32768), (1, "mfma_i8_TOPs", 65536),
+                           (2, "mfma_f8_TOPs", 131072)):
+        ms = _best_ms(lambda: ok(L.pkb_peak_mfma(kind, iters, sink.data_ptr(), grid, st), "mfma"))
+        out[key] = grid * 4 * iters * 8 * per / (ms * 1e-3) / 1e12
+    # Sage runs equal int8 (QK^T) and fp8 (PV) operation counts: its ceiling is
+    # the harmonic mean of the two.
+    out["mfma_i8_f8_half_TOPs"] = 2.0 / (1.0 / out["mfma_i8_TOPs"] + 1.0 / out["mfma_f8_TOPs"])
+    return {k: round(v, 1) for k, v in out.items()}
+
+
 # ---------------------------------------------------------------------------- work counts
 
 def bsa_admitted_pairs(case, use_bits=True):
-    """Admitted (query token, key) pairs summed over query heads."""
+    """Admitted (query token, key) pairs summed over query heads.  use_bits=False
+    leaves validity-bit zeros in (the selected-and-causal count)."""
     B, Sq, Hq, Hkv, D, P, ps = case.dims
     G = Hq // Hkv
     qbs, kvbs = case.q_block_size, case.kv_block_size
@@ -161,6 +278,24 @@ def bsa_admitted_pairs(case, use_bits=True):
     return total * G
 
 
+def bsa_block_area_pairs(case):
+    """Selected blocks x query tokens of the row x keys of the block (no mask):
+    the work a dense-per-block kernel would do."""
+    B, Sq, Hq, Hkv, D, P, ps = case.dims
+    G = Hq // Hkv
+    qbs, kvbs = case.q_block_size, case.kv_block_size
+    total = 0
+    for b in range(B):
+        L = int(case.seq_lens[b])
+        for g in range(Hkv):
+            for r in range(case.block_indptr.shape[2] - 1):
+                blk = np.unique(case.block_indices[case.block_indptr[b, g, r]:case.block_indptr[b, g, r + 1]])
+                rows = min((r + 1) * qbs, Sq) - r * qbs
+                keys = np.clip(blk.astype(np.int64) * kvbs + kvbs, 0, L) - np.clip(blk.astype(np.int64) * kvbs, 0, L)
+                total += rows * int(keys.sum())
+    return total * G
+
+
 def prefill_admitted_pairs(case):
     Hq = case.q.shape[1]
     total = 0
@@ -179,6 +314,7 @@ def prefill_admitted_pairs(case):
 def bench_decode(steps, warmup, W, P):
     log("decode: generating inputs")
     case = W.batch_decode()
+    sha = input_sha256(case.q, case.k, case.v, case.kv_indptr, case.kv_indices, case.seq_lens)
     B, Hq, D = case.q.shape
     Hkv, ps = case.k.shape[1], case.k.shape[2]
     q = case.q.cuda()
@@ -203,19 +339,23 @@ def bench_decode(steps, warmup, W, P):
                        "page_size=16 bf16 (seed 2)",
            "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "page_size": ps,
            "sum_seq_len": int(case.seq_lens.sum()), "num_splits": S, "split_len": split_len,
-           "kv_bytes_per_step": kv_bytes}
+           "kv_bytes_per_step": kv_bytes, "input_sha256": sha}
     kern = ["decode_coop_kernel<128>"] if S == 1 else ["decode_kernel<128>", "decode_merge_kernel<128>"]
-    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(kern, "decode"),
-            "kernel": " + ".join(kern) + " (one step)",
-            "per_unit": "4096 B of K+V per live token (Hkv=8, D=128, bf16)"}
+    gather = PEAKS.get("hbm_gather_4k_GBps")
+    roof = roofline("hbm", ach, "GB/s", HBM_PEAK_GBS, "hbm_read_GBps",
+                    measured_traffic(kern, "decode"), " + ".join(kern) + " (one step)",
+                    per_unit="4096 B of K+V per live token (Hkv=8, D=128, bf16)")
+    if gather:
+        roof["frac_of_measured_4k_gather"] = round(ach / gather, 4)
+    del q, k, v, ws
+    torch.cuda.empty_cache()
     return case, gbs, ms_step, cfg, roof
 
 
 def bench_decode_q(steps, warmup, W, P, SQ=4):
     log(f"decode_q: generating inputs (SQ={SQ})")
     case = W.batch_decode_q(SQ=SQ)
+    sha = input_sha256(case.q, case.k, case.v, case.kv_indptr, case.kv_indices, case.seq_lens)
     B, _, Hq, D = case.q.shape
     Hkv, ps = case.k.shape[1], case.k.shape[2]
     q = case.q.cuda()
@@ -240,17 +380,18 @@ def bench_decode_q(steps, warmup, W, P, SQ=4):
                         "seq_lens~U[512,8192] page_size=16 bf16 (seed 2)",
             "metric": "decode KV-read GB/s", "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
             "unit": "GB/s", "ms_per_step": round(ms_step, 4), "num_splits": S,
-            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "achieved": round(kv_bytes / (ms_launch * 1e-3) / 1e9, 1),
-                         "frac": round(kv_bytes / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(kern, "decode_q"),
-                         "kernel": " + ".join(kern) + " (16 query rows per KV head: 4 tokens x "
-                                   "4 heads)"}}
+            "input_sha256": sha,
+            "roofline": roofline("hbm", kv_bytes / (ms_launch * 1e-3) / 1e9, "GB/s", HBM_PEAK_GBS,
+                                 "hbm_read_GBps", measured_traffic(kern, "decode_q"),
+                                 " + ".join(kern) + " (16 query rows per KV head: 4 tokens x "
+                                 "4 heads)")}
 
 
-def bench_bsa_long(steps, warmup, W, P):
+def bench_bsa_long(steps, warmup, W, P, cpu=False):
     log("long block-sparse: generating inputs")
     case = W.long_bsa()
+    sha = input_sha256(case.q, case.k, case.v, case.kv_indptr, case.kv_indices, case.block_indptr,
+                       case.block_indices, case.seq_lens, case.valid_bits)
     B, Sq, Hq, Hkv, D, Pn, ps = case.dims
     q = case.q.cuda()
     k, v = case.k.cuda(), case.v.cuda()
@@ -267,23 +408,35 @@ def bench_bsa_long(steps, warmup, W, P):
         wr.run(q, (k, v), ip, ix, bip, bix, sl, bits, None, out, lse)
 
     ms_step, ms_launch = time_launches(step, steps, warmup)
-    pairs = bsa_admitted_pairs(case)
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    pairs = bsa_admitted_pairs(case, use_bits=False)       # selected blocks, causal, < L
+    pairs_bits = bsa_admitted_pairs(case, use_bits=True)   # ... and validity bit set
+    area = bsa_block_area_pairs(case)
     flops = 4.0 * D * pairs
     tf = flops / (ms_step * 1e-3) / 1e12
     ach = flops / (ms_launch * 1e-3) / 1e12
-    return {"workload": "long block-sparse paged attention B=4 S=8192 Hq=32 Hkv=8 D=128 "
-                        "page=64 q/kv block 64, 16 blocks/row, causal, 1% invalid bits",
-            "metric": "block-sparse paged attn TFLOP/s (admitted pairs)", "value": round(tf, 2),
-            "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
-            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(["attn_fwd_kernel<128,%d,bsa>" % wr.plan.waves], "bsa"),
-                         "kernel": "attn_fwd_kernel<128,%d,bsa>" % wr.plan.waves}}
+    kname = "attn_fwd_kernel<128,%d,bsa>" % wr.plan.waves
+    r = {"workload": "long block-sparse paged attention B=4 S=8192 Hq=32 Hkv=8 D=128 "
+                     "page=64 q/kv block 64, 16 blocks/row, causal, 1% invalid bits (seed 4)",
+         "metric": "block-sparse paged attn TFLOP/s (selected blocks)", "value": round(tf, 2),
+         "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4),
+         "work": {"admitted_pairs": pairs, "admitted_pairs_valid_bits": pairs_bits,
+                  "block_area_pairs": area,
+                  "counted": "4*D flops per pair of a selected block that passes causal and j < L "
+                             "(validity-bit zeros not subtracted)"},
+         "input_sha256": sha,
+         "roofline": roofline("mfma", ach, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma_bf16_TFLOPs",
+                              measured_traffic([kname], "bsa"), kname)}
+    if cpu:
+        r["cpu_baseline"] = cpu_baseline_bsa(case)
+    return r
 
 
 def bench_prefill(steps, warmup, W, P, D=128, window_left=-1):
     log(f"prefill D={D} w={window_left}: generating inputs")
     case = W.batch_prefill(3, D=D, window_left=window_left)
+    sha = input_sha256(case.q, case.k, case.v, case.qo_indptr, case.block_tables, case.seq_lens)
     q = case.q.cuda()
     k, v = case.k.cuda(), case.v.cuda()
     qo, bt, sl = dev_i32(case.qo_indptr), dev_i32(case.block_tables), dev_i32(case.seq_lens)
@@ -301,20 +454,21 @@ def bench_prefill(steps, warmup, W, P, D=128, window_left=-1):
     flops = 4.0 * D * pairs
     tf = flops / (ms_step * 1e-3) / 1e12
     ach = flops / (ms_launch * 1e-3) / 1e12
+    kname = "attn_fwd_kernel<%d,%d,prefill>" % (D, wr.plan.waves)
     return {"workload": f"batch paged prefill B=8 causal window_left={window_left} Hq=32 "
-                        f"Hkv=8 D={D} page=32 total_q={int(case.qo_indptr[-1])}",
+                        f"Hkv=8 D={D} page=32 total_q={int(case.qo_indptr[-1])} (seed 3)",
             "metric": "paged prefill TFLOP/s (admitted pairs)", "value": round(tf, 2),
             "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
-            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(
-                             ["attn_fwd_kernel<%d,%d,prefill>" % (D, wr.plan.waves)],
-                             "prefill_d%d_w%d" % (D, window_left)),
-                         "kernel": "attn_fwd_kernel<%d,%d,prefill>" % (D, wr.plan.waves)}}
+            "input_sha256": sha,
+            "roofline": roofline("mfma", ach, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma_bf16_TFLOPs",
+                                 measured_traffic([kname], "prefill_d%d_w%d" % (D, window_left)),
+                                 kname)}
 
 
 def bench_bsa_tiny(steps, warmup, W, P):
     case = W.tiny_bsa("causal")
+    sha = input_sha256(case.q, case.k, case.v, case.kv_indptr, case.kv_indices, case.block_indptr,
+                       case.block_indices, case.seq_lens, case.valid_bits)
     B, Sq, Hq, Hkv, D, Pn, ps = case.dims
     q = case.q.cuda()
     k, v = case.k.cuda(), case.v.cuda()
@@ -330,10 +484,10 @@ def bench_bsa_tiny(steps, warmup, W, P):
     ms_step, ms_launch = time_launches(step, steps, warmup)
     pairs = bsa_admitted_pairs(case)
     tf = 4.0 * D * pairs / (ms_step * 1e-3) / 1e12
-    return {"workload": "tiny block-sparse B=2 Sq=64 Hq=4 Hkv=1 D=128 causal (latency-bound)",
+    return {"workload": "tiny block-sparse B=2 Sq=64 Hq=4 Hkv=1 D=128 causal (latency-bound, seed 1)",
             "metric": "block-sparse paged attn TFLOP/s (admitted pairs)", "value": round(tf, 4),
             "unit": "TFLOP/s", "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
-            "us_per_launch": round(ms_launch * 1e3, 2)}
+            "us_per_launch": round(ms_launch * 1e3, 2), "input_sha256": sha}
 
 
 def sage_admitted_pairs(case):
@@ -362,6 +516,8 @@ def sage_admitted_pairs(case):
 def bench_sage(steps, warmup, W, P):
     log("sage: generating inputs")
     case = W.sage_long()
+    sha = input_sha256(case.q_int8, case.k_int8, case.v_fp8, case.q_scale, case.k_scale,
+                       case.v_scale, case.q2k_block_index, case.q2k_block_nums, case.block_sizes)
     q, k, v = case.q_int8.cuda(), case.k_int8.cuda(), case.v_fp8.cuda()
     qs, ks, vs = case.q_scale.cuda(), case.k_scale.cuda(), case.v_scale.cuda()
     idx = dev_i32(case.q2k_block_index)
@@ -377,20 +533,23 @@ def bench_sage(steps, warmup, W, P):
     ops = 4.0 * 128 * pairs
     tops = ops / (ms_step * 1e-3) / 1e12
     ach = ops / (ms_launch * 1e-3) / 1e12
+    roof = roofline("mfma", ach, "TOP/s", INT8_PEAK_TOPS, "mfma_i8_f8_half_TOPs",
+                    measured_traffic(["sage_kernel"], "sage"), "sage_kernel",
+                    frac_of_bf16_peak=round(ach / BF16_PEAK_TFLOPS, 4))
+    if PEAKS.get("mfma_bf16_TFLOPs"):
+        roof["frac_of_measured_bf16_peak"] = round(ach / PEAKS["mfma_bf16_TFLOPs"], 4)
     return {"workload": "Sage block-sparse B=2 H=16 Sq=Sk=16384 D=128 int8 Q/K fp8 V, "
-                        "64 of 256 blocks per query block, last block partial",
+                        "64 of 256 blocks per query block, last block partial (seed 5)",
             "metric": "Sage block-sparse TOP/s (admitted pairs, int8 QK + fp8 PV)",
             "value": round(tops, 2), "unit": "TOP/s", "ms_per_step": round(ms_step, 4),
-            "admitted_pairs": pairs,
-            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS,
-                         "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4),
-                         "frac_of_bf16_peak": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(["sage_kernel"], "sage"), "kernel": "sage_kernel"}}
+            "admitted_pairs": pairs, "input_sha256": sha, "roofline": roof}
 
 
 def bench_qsa(steps, warmup, W, P):
     log("qsa: generating inputs")
     case = W.qsa_long()
+    sha = input_sha256(case.q, case.k, case.v, case.sel_blocks, case.lo, case.hi, case.blk_base,
+                       case.tok_base)
     T, Hq, D = case.q.shape
     Hkv = case.k.shape[1]
     q, k, v = case.q.cuda(), case.k.cuda(), case.v.cuda()
@@ -417,16 +576,22 @@ def bench_qsa(steps, warmup, W, P):
     flops = 4.0 * D * pairs * Hq
     gathered = pairs * Hkv * D * 2 * 2          # K + V rows read per (token, KV head)
     tf = flops / (ms_step * 1e-3) / 1e12
-    ach = flops / (ms_launch * 1e-3) / 1e12
+    ach_tf = flops / (ms_launch * 1e-3) / 1e12
+    ach_gb = gathered / (ms_launch * 1e-3) / 1e9
+    l2 = PEAKS.get("l2_gather_512_GBps")
+    # Bound: gathering one K and one V row of D bf16 per admitted key from L2;
+    # no published figure exists for that rate, so the measured ceiling is the peak.
+    roof = roofline("l2_gather", ach_gb, "GB/s", l2, "l2_gather_512_GBps",
+                    measured_traffic(["qsa_kernel<256>"], "qsa"), "qsa_kernel<256>",
+                    per_unit=f"{Hkv * D * 2 * 2} B of K+V rows gathered per admitted key",
+                    mfma_achieved_TFLOPs=round(ach_tf, 2),
+                    mfma_frac=round(ach_tf / BF16_PEAK_TFLOPS, 4))
     return {"workload": f"packed token-granular sparse attention T={T} (4x4096 causal) Hq={Hq} "
-                        f"Hkv={Hkv} D={D} 4-token blocks, <=64 selected blocks per token",
+                        f"Hkv={Hkv} D={D} 4-token blocks, <=64 selected blocks per token (seed 7)",
             "metric": "QSA TFLOP/s (admitted pairs)", "value": round(tf, 2), "unit": "TFLOP/s",
             "ms_per_step": round(ms_step, 4), "admitted_pairs": pairs,
-            "gathered_kv_GBps": round(gathered / (ms_launch * 1e-3) / 1e9, 1),
-            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(["qsa_kernel<256>"], "qsa"),
-                         "kernel": "qsa_kernel<256>"}}
+            "gathered_kv_GBps": round(gathered / (ms_step * 1e-3) / 1e9, 1),
+            "input_sha256": sha, "roofline": roof}
 
 
 def bench_copy():
@@ -442,30 +607,296 @@ def bench_copy():
     return {"workload": "device copy", "bytes_per_copy": n, "copies": 3}
 
 
-def cpu_baseline_decode(case, budget_s=15.0):
-    """fp64 oracle on the first requests of the decode batch until ~budget_s."""
-    from oracle import attention as A
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    done, nbytes = [], 0
-    Hkv, D = case.k.shape[1], case.k.shape[3]
-    t0 = time.perf_counter()
-    for b in range(len(case.seq_lens)):
-        A.decode_reference(case.q, case.k, case.v, case.kv_indptr, case.kv_indices,
-                           case.seq_lens, requests=[b])
-        done.append(b)
-        nbytes += int(case.seq_lens[b]) * Hkv * D * 2 * 2
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"fp64 NumPy oracle over requests {done[0]}..{done[-1]} "
-                      f"({len(done)} of 64, {nbytes} live K+V bytes) in {dt:.1f} s"}
+# ---------------------------------------------------------------------------- CPU oracle baseline
+#
+# The fp64 oracle runs in worker processes, one per host core (one BLAS thread
+# each).  The inputs sit in shared memory; each task takes one request's pages
+# (decode) or one BSR row's query tokens and its request's pages for one KV
+# head (block-sparse), and runs the oracle on exactly that data.
 
+_SHM = {}
+
+
+def _shm_put(name, arr):
+    from multiprocessing import shared_memory
+    arr = np.ascontiguousarray(arr)
+    shm = shared_memory.SharedMemory(create=True, size=max(arr.nbytes, 1))
+    np.ndarray(arr.shape, arr.dtype, buffer=shm.buf)[...] = arr
+    _SHM[name] = shm
+    return (shm.name, arr.shape, arr.dtype.str)
+
+
+def _shm_view(desc):
+    from multiprocessing import shared_memory
+    name, shape, dt = desc
+    shm = shared_memory.SharedMemory(name=name)
+    _SHM[name] = shm                       # keep the mapping alive in the worker
+    return np.ndarray(shape, np.dtype(dt), buffer=shm.buf)
+
+
+_W = {}
+
+
+def _worker_init(descs):
+    for k, d in descs.items():
+        _W[k] = _shm_view(d)
+
+
+def _worker_ready(_):
+    from oracle import attention  # noqa: F401  (import before the timed region)
+    return os.getpid()
+
+
+def _bf16_bits_to_f32(u16):
+    return (u16.astype(np.uint32) << 16).view(np.float32)
+
+
+def _decode_task(b):
+    from oracle import attention as A
+    ip, ix, sl = _W["indptr"], _W["indices"], _W["seq_lens"]
+    pages = ix[ip[b]:ip[b + 1]]
+    n = len(pages)
+    kb = _bf16_bits_to_f32(_W["k"][pages])
+    vb = _bf16_bits_to_f32(_W["v"][pages])
+    qb = _bf16_bits_to_f32(_W["q"][b:b + 1])
+    A.decode_reference(qb, kb, vb, np.array([0, n]), np.arange(n), sl[b:b + 1])
+    return b
+
+
+def _bsa_task(t):
+    from oracle import attention as A
+    b, g, r = t
+    ip, ix = _W["indptr"], _W["indices"]
+    bip, bix, sl, bits = _W["block_indptr"], _W["block_indices"], _W["seq_lens"], _W["bits"]
+    q = _W["q"]
+    Sq, G, qbs = q.shape[1], q.shape[2] // _W["k"].shape[1], 64
+    pages = ix[ip[b]:ip[b + 1]]
+    n = len(pages)
+    kb = _bf16_bits_to_f32(_W["k"][pages, g:g + 1])
+    vb = _bf16_bits_to_f32(_W["v"][pages, g:g + 1])
+    rows = np.arange(r * qbs, min((r + 1) * qbs, Sq))
+    qm = np.zeros((1, Sq, G, q.shape[3]), np.float32)
+    qm[0, rows] = _bf16_bits_to_f32(q[b, rows, g * G:(g + 1) * G])
+    sel = bix[bip[b, g, r]:bip[b, g, r + 1]]
+    nqb = bip.shape[2] - 1
+    bipm = np.where(np.arange(nqb + 1) <= r, 0, len(sel)).astype(np.int64).reshape(1, 1, nqb + 1)
+    A.bsa_reference(qm, kb, vb, np.array([0, n]), np.arange(n), bipm, sel, qbs, 64,
+                    sl[b:b + 1], valid_bits=bits[b:b + 1], mask="causal",
+                    tokens=[(0, int(i)) for i in rows])
+    return t
+
+
+def _cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{cfg.get('name')} {cfg.get('version')}"
+    except Exception:  # pragma: no cover
+        pass
+    return model, blas
+
+
+def _run_pool(descs, fn, tasks):
+    """Wall time of fn over tasks in worker processes (one per host core, one
+    BLAS thread each), started and warmed before the clock starts."""
+    import multiprocessing as mp
+    if any(k.startswith(("ROCPROF", "ROCP_")) for k in os.environ):
+        # Worker processes would inherit the profiler's preloaded tool, which
+        # attaches to the GPU in every child: never run the pool under it.
+        raise RuntimeError("the CPU baseline does not run under a profiler "
+                           "(pass --no-cpu-baseline)")
+    cores = len(os.sched_getaffinity(0))
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                            "MKL_NUM_THREADS", "HIP_VISIBLE_DEVICES",
+                                            "ROCR_VISIBLE_DEVICES", "CUDA_VISIBLE_DEVICES")}
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[k] = "1"
+    for k in ("HIP_VISIBLE_DEVICES", "ROCR_VISIBLE_DEVICES", "CUDA_VISIBLE_DEVICES"):
+        os.environ[k] = ""          # the workers never touch a GPU
+    try:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(cores, initializer=_worker_init, initargs=(descs,)) as pool:
+            pool.map(_worker_ready, range(cores), chunksize=1)
+            t0 = time.perf_counter()
+            pool.map(fn, tasks, chunksize=1)
+            dt = time.perf_counter() - t0
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return dt, cores
+
+
+def _shm_release():
+    for shm in _SHM.values():
+        try:
+            shm.close()
+            shm.unlink()
+        except FileNotFoundError:
+            pass
+    _SHM.clear()
+
+
+def _u16(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_baseline_decode(case):
+    """The fp64 oracle over the whole decode batch (64 requests)."""
+    try:
+        descs = {"q": _shm_put("q", _u16(case.q)), "k": _shm_put("k", _u16(case.k)),
+                 "v": _shm_put("v", _u16(case.v)), "indptr": _shm_put("ip", case.kv_indptr),
+                 "indices": _shm_put("ix", case.kv_indices),
+                 "seq_lens": _shm_put("sl", case.seq_lens)}
+        B = len(case.seq_lens)
+        order = sorted(range(B), key=lambda b: -int(case.seq_lens[b]))   # longest first
+        dt, cores = _run_pool(descs, _decode_task, order)
+    finally:
+        _shm_release()
+    Hkv, D = case.k.shape[1], case.k.shape[3]
+    nbytes = int(case.seq_lens.astype(np.int64).sum()) * Hkv * D * 2 * 2
+    model, blas = _cpu_info()
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle over all {B} requests of the decode batch "
+                      f"({nbytes} live K+V bytes) in {dt:.2f} s wall, {cores} worker processes "
+                      "with one BLAS thread each",
+            "cpu_model": model, "blas": blas}
+
+
+def cpu_baseline_bsa(case, heads_per_row=2):
+    """The fp64 oracle over a sample of the long block-sparse work: every BSR
+    row of every request, `heads_per_row` of its KV heads (rotating)."""
+    B, Sq, Hq, Hkv, D, Pn, ps = case.dims
+    nqb = case.block_indptr.shape[2] - 1
+    tasks = [(b, (b * 3 + r + k * Hkv // heads_per_row) % Hkv, r) for b in range(B)
+             for r in range(nqb) for k in range(heads_per_row)]
+    G = Hq // Hkv
+    pairs = 0
+    for b, g, r in tasks:     # selected-and-causal pairs of the row (the GPU headline's count)
+        L = int(case.seq_lens[b])
+        blk = np.unique(case.block_indices[case.block_indptr[b, g, r]:case.block_indptr[b, g, r + 1]])
+        p = L - Sq + np.arange(r * 64, min(r * 64 + 64, Sq))
+        a0 = np.clip(blk.astype(np.int64) * 64, 0, L)[None, :]
+        a1 = np.clip(blk.astype(np.int64) * 64 + 64, 0, L)[None, :]
+        hi = np.minimum(a1, (p + 1)[:, None])
+        pairs += int(np.maximum(hi - a0, 0).sum()) * G
+    try:
+        descs = {"q": _shm_put("q", _u16(case.q)), "k": _shm_put("k", _u16(case.k)),
+                 "v": _shm_put("v", _u16(case.v)), "indptr": _shm_put("ip", case.kv_indptr),
+                 "indices": _shm_put("ix", case.kv_indices),
+                 "block_indptr": _shm_put("bip", case.block_indptr),
+                 "block_indices": _shm_put("bix", case.block_indices),
+                 "seq_lens": _shm_put("sl", case.seq_lens), "bits": _shm_put("bits", case.valid_bits)}
+        dt, cores = _run_pool(descs, _bsa_task, tasks)
+    finally:
+        _shm_release()
+    model, blas = _cpu_info()
+    flops = 4.0 * D * pairs
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle over {len(tasks)} of {B * Hkv * nqb} (request, KV head, "
+                      f"BSR row) units (every row, {heads_per_row} of {Hkv} KV heads each; {pairs} "
+                      f"admitted pairs) in {dt:.2f} s wall, {cores} worker processes with one BLAS "
+                      "thread each",
+            "cpu_model": model, "blas": blas}
+
+
+# ---------------------------------------------------------------------------- trace summaries
+
+def trace_summary(path, last):
+    """Markdown table of a rocprofv3 kernel trace (kernel_trace.csv): per
+    kernel, the dispatch count and mean duration over all dispatches and over
+    the last `last` dispatches (bench's timed launches, after its warmup)."""
+    import csv
+    durs = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            durs.setdefault(row["Kernel_Name"], []).append((int(row["Start_Timestamp"]), d))
+    lines = ["| kernel | dispatches | mean, all (us) | timed dispatches | mean, timed (us) | min (us) |",
+             "|---|---|---|---|---|---|"]
+    for name, xs in sorted(durs.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        xs.sort()
+        ds = [d for _, d in xs]
+        tail = ds[-last:] if len(ds) > last else ds
+        lines.append(f"| `{name}` | {len(ds)} | {np.mean(ds):.2f} | {len(tail)} | "
+                     f"{np.mean(tail):.2f} | {min(tail):.2f} |")
+    return "\n".join(lines)
+
+
+def pmc_summary(path, last, num_cus=256, xcds=8):
+    """Markdown table of a rocprofv3 counter collection (counter_collection.csv):
+    per kernel, each counter's mean over its last `last` dispatches, and the
+    derived figures.  GRBM_GUI_ACTIVE counts every XCD's cycles (their sum), so
+    the kernel's clock is GRBM_GUI_ACTIVE / xcds / duration, and the share of
+    SIMD cycles the matrix pipe is busy is
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / xcds * num_cus * 4)."""
+    import csv
+    vals, durs = {}, {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            k, did = row["Kernel_Name"], int(row["Dispatch_Id"])
+            vals.setdefault(k, {}).setdefault(row["Counter_Name"], {})[did] = float(row["Counter_Value"])
+            durs.setdefault(k, {})[did] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+    out = []
+    for k, cs in vals.items():
+        if k.startswith("__amd_rocclr") or "at::native" in k:
+            continue
+        ids = sorted(durs[k])[-last:]
+        mean = {c: float(np.mean([v[i] for i in ids if i in v])) for c, v in cs.items()}
+        dur = float(np.mean([durs[k][i] for i in ids]))
+        out.append(f"**`{k}`** -- {len(ids)} dispatches, mean duration {dur:.2f} us")
+        out.append("")
+        out.append("| counter | mean per dispatch |")
+        out.append("|---|---|")
+        for c in sorted(mean):
+            out.append(f"| {c} | {mean[c]:,.0f} |")
+        gui = mean.get("GRBM_GUI_ACTIVE")
+        derived = []
+        if gui:
+            cyc = gui / xcds
+            derived.append(("clock (GHz)", f"{cyc / (dur * 1e3):.3f}"))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                derived.append(("matrix pipe busy (share of SIMD cycles)",
+                                f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * num_cus * 4):.4f}"))
+            for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_LDS",
+                      "SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                      "SQ_WAVE_CYCLES", "SQ_LDS_IDX_ACTIVE"):
+                if c in mean:
+                    derived.append((f"{c} / (SIMD cycles)", f"{mean[c] / (cyc * num_cus * 4):.4f}"))
+        mf = mean.get("SQ_INSTS_MFMA")
+        if mf:
+            if "SQ_INSTS_VALU" in mean:
+                derived.append(("non-MFMA VALU instructions per MFMA",
+                                f"{(mean['SQ_INSTS_VALU'] - mf) / mf:.2f}"))
+            for c in ("SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_SMEM"):
+                if c in mean:
+                    derived.append((f"{c} per MFMA", f"{mean[c] / mf:.2f}"))
+        for c, per in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", 512), ("SQ_INSTS_VALU_MFMA_MOPS_I8", 512),
+                       ("SQ_INSTS_VALU_MFMA_MOPS_F8", 512)):
+            if mean.get(c):
+                derived.append((f"{c} x {per} (matrix ops executed)", f"{mean[c] * per:.4e}"))
+        if derived:
+            out.append("")
+            out.append("| derived | value |")
+            out.append("|---|---|")
+            out += [f"| {a} | {b} |" for a, b in derived]
+        out.append("")
+    return "\n".join(out)
+
+
+# ---------------------------------------------------------------------------- main
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
@@ -476,10 +907,25 @@ def main(argv=None):
                          "on until 0.2 s of untimed work has run)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["decode", "decode_q", "bsa", "prefill", "prefill_w1024", "prefill256", "tiny",
-                                       "sage", "qsa", "copy"], default=None,
-                    help="run one workload only (for profiling; copy = counter calibration)")
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--only", choices=["decode", "decode_q", "bsa", "prefill", "prefill_w1024",
+                                       "prefill256", "tiny", "sage", "qsa", "copy", "peaks"],
+                    default=None,
+                    help="run one workload only (for profiling; copy = counter calibration, "
+                         "peaks = the on-device ceilings)")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV", default=None,
+                    help="print a markdown summary of a rocprofv3 kernel trace and exit (mean "
+                         "over the last 2*steps dispatches of each kernel: the timed ones)")
+    ap.add_argument("--pmc-summary", metavar="COUNTER_COLLECTION_CSV", default=None,
+                    help="print a markdown summary of a rocprofv3 counter collection and exit "
+                         "(means over the last 2*steps dispatches of each kernel)")
     a = ap.parse_args(argv)
+    if a.trace_summary:
+        print(trace_summary(a.trace_summary, 2 * a.steps))
+        return 0
+    if a.pmc_summary:
+        print(pmc_summary(a.pmc_summary, 2 * a.steps))
+        return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU component "
               "(run with --gpus 1)", file=sys.stderr)
@@ -491,7 +937,21 @@ def main(argv=None):
     from gen import workloads as W
     import paged_kv_block_amd as P
 
-    if a.only and a.only != "decode":
+    if a.only == "peaks" or (a.only is None and not a.no_peaks):
+        log("peaks: measuring on-device ceilings")
+        PEAKS.update(measure_peaks(P))
+        log(f"peaks: {PEAKS}")
+        if a.only == "peaks":
+            print(json.dumps({"peaks": PEAKS}), flush=True)
+            return 0
+
+    if a.only:
+        if a.only == "decode":
+            case, gbs, ms_step, cfg, roof = bench_decode(a.steps, a.warmup, W, P)
+            print(json.dumps({"metric": "decode KV-read GB/s", "value": round(gbs, 1),
+                              "unit": "GB/s", "ms_per_step": round(ms_step, 4), "config": cfg,
+                              "roofline": roof}), flush=True)
+            return 0
         fn = {"bsa": lambda: bench_bsa_long(a.steps, a.warmup, W, P),
               "prefill": lambda: bench_prefill(a.steps, a.warmup, W, P),
               "prefill_w1024": lambda: bench_prefill(a.steps, a.warmup, W, P, window_left=1024),
@@ -508,7 +968,7 @@ def main(argv=None):
     log(f"decode: {gbs:.1f} GB/s, {ms_step * 1e3:.1f} us/step")
     secondary = []
     if not a.no_secondary and a.only is None:
-        for fn in (lambda: bench_bsa_long(a.steps, a.warmup, W, P),
+        for fn in (lambda: bench_bsa_long(a.steps, a.warmup, W, P, cpu=not a.no_cpu_baseline),
                    lambda: bench_prefill(a.steps, a.warmup, W, P),
                    lambda: bench_prefill(a.steps, a.warmup, W, P, window_left=1024),
                    lambda: bench_prefill(a.steps, a.warmup, W, P, D=256),
@@ -522,13 +982,14 @@ def main(argv=None):
             torch.cuda.empty_cache()
     cpu = None
     if not a.no_cpu_baseline:
-        log("cpu baseline: timing the oracle")
+        log("cpu baseline: timing the oracle on the decode batch")
         cpu = cpu_baseline_decode(case)
     line = {"metric": "decode KV-read GB/s", "value": round(gbs, 1), "unit": "GB/s",
             "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
             "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16)",
-            "config": cfg, "roofline": roof, "cpu_baseline": cpu, "secondary": secondary}
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+            "peaks": PEAKS or None, "secondary": secondary}
     print(json.dumps(line), flush=True)
     return 0
 

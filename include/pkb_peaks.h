@@ -1,0 +1,54 @@
+/*
+ * pkb_peaks.h -- C ABI of libpkb_peaks.so: on-device ceilings of an MI355X
+ * (gfx950) used as measured roofline denominators next to the published ones.
+ * Measurement code only; nothing here is part of the attention path.
+ *
+ * Every function enqueues one kernel on `stream` (a hipStream_t passed as
+ * void*; NULL = the default stream) and returns 0, or a negative HIP error
+ * code when the arguments are out of range or the launch fails.  Buffers are
+ * caller-owned device memory; the kernels only read them, apart from `sink`
+ * (at least 16 bytes), which receives a value only when a checksum hits a
+ * fixed constant (it exists so that no load or MFMA can be removed).
+ * `grid` is the number of 256-thread workgroups.
+ */
+#ifndef PKB_PEAKS_H_
+#define PKB_PEAKS_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Streaming read of `bytes` (a multiple of 4096) from `buf`: every byte once;
+ * consecutive waves read consecutive 4 KiB chunks, each wave keeping four
+ * chunks (16 loads of 16 bytes per lane) in flight. */
+int pkb_peak_hbm_read(const void* buf, int64_t bytes, void* sink, int32_t grid, void* stream);
+
+/* Gather of `n_reads` slabs of 4096 bytes at pseudo-random slab indices of
+ * `buf` (`bytes` a multiple of 4096, at least one slab): the access shape of
+ * paged decode (one 16-token page of one KV head at D = 128).  Each wave keeps
+ * four slabs in flight; n_reads is rounded up to whole wave iterations
+ * (returned bytes = 4096 * reads actually made, written to *bytes_read). */
+int pkb_peak_hbm_gather(const void* buf, int64_t bytes, int64_t n_reads, void* sink,
+                        int32_t grid, int64_t* bytes_read, void* stream);
+
+/* Gather of 512-byte rows at pseudo-random row indices of a buffer small
+ * enough to stay in each XCD's 4 MB L2 (`bytes` a multiple of 512, at most
+ * 4 MiB): the access shape of the packed-query sparse kernel (one K or V row
+ * of 256 bf16).  Reads `n_reads` rows in total (rounded up as above). */
+int pkb_peak_l2_gather(const void* buf, int64_t bytes, int64_t n_reads, void* sink,
+                       int32_t grid, int64_t* bytes_read, void* stream);
+
+/* Dense MFMA loop: every wave issues `iters` rounds of 8 independent
+ * accumulations.  kind 0: v_mfma_f32_32x32x16_bf16 (32768 flop each);
+ * 1: v_mfma_i32_32x32x32_i8 (65536 op); 2: v_mfma_f32_32x32x64_f8f6f4 with
+ * fp8 E4M3 operands (131072 op).  Total operations = grid * 4 waves * iters *
+ * 8 * (operations per instruction). */
+int pkb_peak_mfma(int32_t kind, int32_t iters, void* sink, int32_t grid, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKB_PEAKS_H_ */

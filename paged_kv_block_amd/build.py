@@ -1,4 +1,6 @@
-"""Build libpkb.so in-tree for gfx950 (explicit hipcc / g++ invocations).
+"""Build libpkb.so (the attention library) and libpkb_peaks.so (on-device
+ceilings used by the benchmark) in-tree for gfx950 (explicit hipcc / g++
+invocations).
 
 Usage: python paged_kv_block_amd/build.py [-j N]   (run by path: importing the
 package loads the library this script builds)
@@ -17,6 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpkb.so")
+PEAKS_LIB = os.path.join(HERE, "libpkb_peaks.so")
 
 ARCH = os.environ.get("PKB_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -32,6 +35,7 @@ SOURCE_FLAGS = {"decode_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "qsa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 CPP_SOURCES = ["host.cpp"]
+PEAKS_SOURCES = ["peaks.hip"]
 
 
 def _run(cmd):
@@ -44,7 +48,7 @@ def _run(cmd):
 def compile_one(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
-    if src in HIP_SOURCES:
+    if src in HIP_SOURCES or src in PEAKS_SOURCES:
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-x", "hip", "-c", path, "-o", obj,
                *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []),
                "-Wno-unused-command-line-argument"]
@@ -56,14 +60,16 @@ def compile_one(src: str) -> str:
 
 def build(jobs: int = 4, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = HIP_SOURCES + CPP_SOURCES
+    srcs = HIP_SOURCES + CPP_SOURCES + PEAKS_SOURCES
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+        objs = dict(zip(srcs, ex.map(compile_one, srcs)))
+    for lib, group in ((LIB, HIP_SOURCES + CPP_SOURCES), (PEAKS_LIB, PEAKS_SOURCES)):
+        tmp = lib + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[objs[x] for x in group],
+              "-o", tmp])
+        os.replace(tmp, lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 

@@ -22,8 +22,8 @@ from oracle import metadata as M
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def header_functions():
-    txt = open(os.path.join(ROOT, "include", "pkb.h")).read()
+def header_functions(header="pkb.h"):
+    txt = open(os.path.join(ROOT, "include", header)).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", txt, flags=re.M)))
 
@@ -40,6 +40,19 @@ def test_every_declared_symbol_is_exported():
     L = P.lib()
     for n in names:
         assert hasattr(L, n)
+
+
+def test_peaks_library_exports_its_header():
+    """libpkb_peaks.so (the on-device ceilings the benchmark measures) exports
+    every function include/pkb_peaks.h declares."""
+    names = header_functions("pkb_peaks.h")
+    assert names == ["pkb_peak_hbm_gather", "pkb_peak_hbm_read", "pkb_peak_l2_gather",
+                     "pkb_peak_mfma"]
+    lib = os.path.join(ROOT, "paged_kv_block_amd", "libpkb_peaks.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    assert set(names) <= exported
 
 
 def test_status_strings_and_version():

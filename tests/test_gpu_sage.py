@@ -75,6 +75,8 @@ def test_sage_no_block_sizes_and_full_selection():
 
 
 def test_sage_long_sampled():
+    """Full-size Sage workload: every query block of (b=1, h=7) and sampled
+    blocks elsewhere."""
     case = W.sage_long()
     _say("sage_long: generated")
     out = run_sage(case)
@@ -82,6 +84,7 @@ def test_sage_long_sampled():
     rows = [(int(b), int(h), int(r)) for b, h, r in
             zip(rng.integers(0, 2, 6), rng.integers(0, 16, 6), rng.integers(0, 256, 6))]
     rows += [(0, 0, 0), (1, 15, 255)]
+    rows += [(1, 7, r) for r in range(256)]          # one whole (request, head)
     ref = oracle(case, rows=rows)
     got = f64(out)
     for b, h, r in rows:

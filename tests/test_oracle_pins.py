@@ -625,3 +625,86 @@ def test_qsa_partition_spans():
     assert tb.tolist() == [0] * 7 + [7] * 4 + [11]
     assert bb.tolist() == [0] * 7 + [2] * 4 + [3]
     assert bf.tolist() == [0, 4, 7, 11] and bl.tolist() == [3, 6, 10, 11]
+
+
+# ---------------------------------------------------------------------------
+# row-subset selectors (the full-size GPU tests compare sampled rows through
+# them): each equals the matching slice of the full result
+# ---------------------------------------------------------------------------
+
+def test_prefill_rows_selector_is_slice_of_full():
+    case = W.make_prefill(31, 3, [37, 5, 70], [10, 0, 33], 4, 2, 16, 16, mask="causal",
+                          window_left=20)
+    args = (case.q, case.k, case.v, case.qo_indptr, case.block_tables, case.seq_lens)
+    o, l = A.prefill_reference(*args, mask="causal", window_left=20)
+    rows = [111, 0, 36, 37, 41, 42, 75, 3]        # unsorted, request boundaries
+    os_, ls_ = A.prefill_reference(*args, mask="causal", window_left=20, rows=rows)
+    cmp(os_, o[rows], 1e-12)
+    cmp(ls_, l[rows], 1e-12)
+    # rows past a chunk boundary of the selector's batching
+    o2, l2 = A.prefill_reference(*args, mask="causal", window_left=20, rows=list(range(112)),
+                                 chunk=7)
+    cmp(o2, o, 1e-12)
+    cmp(l2, l, 1e-12)
+
+
+def test_decode_requests_selector_is_slice_of_full():
+    case = W.make_decode(32, 5, 8, 2, 16, [40, 1, 77, 16, 5], 8, mask="causal", window_left=9)
+    args = (case.q, case.k, case.v, case.kv_indptr, case.kv_indices, case.seq_lens)
+    o, l = A.decode_reference(*args, mask="causal", window_left=9, bmm2_scale=0.7)
+    reqs = [4, 0, 2, 2]
+    os_, ls_ = A.decode_reference(*args, mask="causal", window_left=9, bmm2_scale=0.7,
+                                  requests=reqs)
+    cmp(os_, o[reqs], 1e-12)
+    cmp(ls_, l[reqs], 1e-12)
+
+
+def test_sage_rows_selector_is_slice_of_full():
+    case = W.make_sage(33, 2, 2, 200, 300, 4, count_lo=0, block_sizes_rank=3)
+    codes = case.v_fp8.view(torch.uint8).numpy()
+    args = (case.q_int8, case.k_int8, codes, case.q_scale, case.k_scale, case.v_scale,
+            case.q2k_block_index, case.block_sparse_num, case.block_sizes, case.q2k_block_nums)
+    for mask in ("dense", "causal"):
+        o, l = A.sage_reference(*args, Sk=case.Sk, mask=mask, with_lse=True)
+        rows = [(1, 0, 3), (0, 1, 0), (1, 1, 2)]
+        os_, ls_ = A.sage_reference(*args, Sk=case.Sk, mask=mask, with_lse=True, rows=rows)
+        for b, h, r in rows:
+            sl = slice(64 * r, min(64 * r + 64, 200))
+            cmp(os_[b, h, sl], o[b, h, sl], 1e-12)
+            cmp(ls_[b, h, sl], l[b, h, sl], 1e-12)
+        # everything outside the selected rows is left unset
+        keep = np.zeros((2, 2, 200), bool)
+        for b, h, r in rows:
+            keep[b, h, 64 * r:64 * r + 64] = True
+        assert np.isnan(os_[~keep]).all() and np.isnan(ls_[~keep]).all()
+
+
+def test_qsa_tokens_selector_is_slice_of_full():
+    case = W.make_qsa(34, [9, 14, 7], Hq=4, Hkv=2, D=16, p_sel=0.4, empty_rows=2)
+    args = (case.q, case.k, case.v, case.sel_blocks, case.lo, case.hi, case.block_first,
+            case.block_last, case.scale)
+    o, l = A.qsa_reference(*args)
+    toks = [29, 0, 13, 9, 8]
+    os_, ls_ = A.qsa_reference(*args, tokens=toks)
+    cmp(os_[toks], o[toks], 1e-12)
+    cmp(ls_[:, toks], l[:, toks], 1e-12)
+    rest = np.setdiff1d(np.arange(30), toks)
+    assert np.isnan(os_[rest]).all() and np.isnan(ls_[:, rest]).all()
+
+
+def test_sage_uniform_count_ignores_per_row_counts():
+    """Sage page (Parameters): with uniform_block_count set every row uses
+    block_sparse_num and the per-row counts are ignored -- the same result as
+    passing no counts at all, and different from honouring the counts."""
+    case = W.make_sage(35, 1, 2, 130, 400, 5, nsel=3, count_lo=0, block_sizes_rank=1)
+    codes = case.v_fp8.view(torch.uint8).numpy()
+    base = (case.q_int8, case.k_int8, codes, case.q_scale, case.k_scale, case.v_scale,
+            case.q2k_block_index, 3, case.block_sizes)
+    assert (case.q2k_block_nums != 3).any()
+    o_uni = A.sage_reference(*base, case.q2k_block_nums, uniform_block_count=True, Sk=case.Sk)
+    o_none = A.sage_reference(*base, None, Sk=case.Sk)
+    o_rows = A.sage_reference(*base, case.q2k_block_nums, uniform_block_count=False, Sk=case.Sk)
+    cmp(o_uni, o_none, 0.0)
+    differ = [(0, h, r) for h in range(2) for r in range(3) if case.q2k_block_nums[0, h, r] != 3]
+    assert any(not np.allclose(o_uni[0, h, 64 * r:64 * r + 64], o_rows[0, h, 64 * r:64 * r + 64])
+               for _, h, r in differ)
