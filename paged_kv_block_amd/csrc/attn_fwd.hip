@@ -255,13 +255,22 @@ attn_fwd_kernel(const AttnParams p) {
     k_hi = min(k_hi, (split + 1) * p.split_len);
   }
 
-  // visited KV: contiguous modes walk [lo8, k_hi) in 64-token tiles; sparse
-  // rows walk their selected blocks in order, 8-token chunks packed 8 per tile
+  // Chunks (8 tokens) this wave copies per tile, and their token span.  When
+  // every wave's span of a tile lies inside one page -- contiguous walks whose
+  // tiles start on a multiple of the span, with page_size a multiple of it --
+  // each tile's copy sources come from lane-parallel descriptors (below).
+  constexpr int CPW = 8 / NW;
+  constexpr int SPAN = 8 * CPW;
+  const bool fast = CONTIG && p.page_size % SPAN == 0;
+
+  // visited KV: contiguous modes walk [lo8, k_hi) in 64-token tiles (lo8 a
+  // multiple of 8, and of SPAN on the fast path); sparse rows walk their
+  // selected blocks in order, 8-token chunks packed 8 per tile
   int n_tiles, lo8 = 0;
   if (MODE == kModeBsa) {
     n_tiles = CONTIG ? n_sel * (p.kvbs >> 6) : (n_sel * (p.kvbs >> 3) + 7) >> 3;
   } else {
-    lo8 = k_lo & ~7;
+    lo8 = k_lo & (fast ? -SPAN : -8);
     n_tiles = (k_hi > k_lo) ? (k_hi - lo8 + 63) >> 6 : 0;
   }
 
@@ -291,8 +300,45 @@ attn_fwd_kernel(const AttnParams p) {
     return ld_const(p.block_indices, bip_lo + qq) * p.kvbs + (v - (qq << cpb_sh)) * 8;
   };
 
-  constexpr int CPW = 8 / NW;
   using TM = TileMeta<CPW>;
+
+  // Lane-parallel tile descriptors (fast path): lane l describes tile
+  // j0 + l -- its first token, the pool offset of this wave's SPAN tokens (a
+  // span at or past L, whose pages may not exist, is redirected to the last
+  // live span; the copies of such rows are never used), and for block-sparse
+  // tiles the two validity words of its 64 keys.  The tile loop reads them with
+  // v_readlane instead of a chain of dependent scalar loads, divisions by the
+  // page size and 64-bit products per tile.
+  int d_t0 = 0;
+  int64_t d_src = 0;
+  uint32_t d_w0 = ~0u, d_w1 = ~0u;
+  auto load_desc = [&](int j0) {
+    const int j = j0 + lane;
+    const bool live = j < n_tiles;
+    int t0 = 0;
+    if (live) {
+      if (MODE == kModeBsa) {
+        const int qq = bt_pow2 ? (j >> bt_sh) : j / blk_tiles;
+        t0 = p.block_indices[bip_lo + qq] * p.kvbs + (j - qq * blk_tiles) * 64;
+      } else {
+        t0 = lo8 + 64 * j;
+      }
+    }
+    d_t0 = t0;
+    int tw = t0 + SPAN * wave;
+    if (tw >= L) tw = max((L - 1) & -SPAN, 0);
+    const int pi = ps_pow2 ? (tw >> ps_sh) : tw / p.page_size;
+    const int id = live ? ids[pi] : 0;
+    d_src = (int64_t)id * p.kv_page_stride + head_off + (int64_t)(tw - pi * p.page_size) * D;
+    if (MODE == kModeBsa && p.valid_bits) {
+      // keys t0..t0+63 are two whole words; the second is read only when it
+      // exists in the row (its bits are used only when t0 + 32 < L)
+      const int64_t w = (int64_t)b * p.valid_words + (t0 >> 5);
+      d_w0 = live ? p.valid_bits[w] : 0u;
+      d_w1 = (live && (t0 >> 5) + 1 < p.valid_words) ? p.valid_bits[w + 1] : 0u;
+    }
+  };
+  if (fast && n_tiles > 0) load_desc(0);
   // pool offsets of the chunks this wave copies (tm.tsrc set)
   auto fill_src = [&](TM& tm) {
     int pi[CPW], id[CPW];
@@ -311,7 +357,38 @@ attn_fwd_kernel(const AttnParams p) {
   };
   auto tile_meta = [&](int j) -> TM {
     TM tm;
-    if (CONTIG) {
+    if (CONTIG && fast) {
+      const int jj = j & 63;
+      if (jj == 0 && j > 0) load_desc(j);   // next 64 tiles (rare)
+      const int t0 = readlane_i32(d_t0, jj);
+      const int lo = min(max(k_lo - t0, 0), 64);
+      const int hi = min(max(k_hi - t0, 0), 64);
+      uint64_t M = (hi >= 64 ? ~0ull : ((1ull << hi) - 1ull)) & ~(lo >= 64 ? ~0ull : ((1ull << lo) - 1ull));
+      if (MODE == kModeBsa && p.valid_bits && M) {
+        const uint32_t w0 = (uint32_t)readlane_i32((int)d_w0, jj);
+        const uint32_t w1 = (uint32_t)readlane_i32((int)d_w1, jj);
+        M &= (uint64_t)w0 | ((t0 + 32 < L) ? (uint64_t)w1 << 32 : 0ull);
+      }
+      tm.M = M;
+      tm.t0 = t0;
+      const int c_first = M ? (__builtin_ctzll(M) >> 3) : 0;
+      const int c_last = M ? ((63 - __builtin_clzll(M)) >> 3) : 0;
+      tm.tmin = t0 + 8 * c_first;
+      tm.tmax = t0 + 8 * c_last + 7;
+      if (M) {
+        // the span's first chunk is live (tw < L); a chunk at or past L copies
+        // it instead, so LDS never holds what lies past the sequence
+        int tw = t0 + SPAN * wave;
+        if (tw >= L) tw = max((L - 1) & -SPAN, 0);
+        const int64_t src = readlane_i64(d_src, jj);
+#pragma unroll
+        for (int lc = 0; lc < CPW; ++lc) {
+          const bool live = tw + 8 * lc < L;
+          tm.tsrc[lc] = live ? tw + 8 * lc : tw;
+          tm.src[lc] = live ? src + (int64_t)(8 * lc) * D : src;
+        }
+      }
+    } else if (CONTIG) {
       int t0;
       if (MODE == kModeBsa) {
         const int qq = bt_pow2 ? (j >> bt_sh) : j / blk_tiles;
