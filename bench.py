@@ -896,6 +896,90 @@ def pmc_summary(path, last, num_cus=256, xcds=8):
     return "\n".join(out)
 
 
+# Kernel short names and the sources each one is built from (a traffic record
+# is valid only while these files are unchanged).
+_KERNEL_SOURCES = {
+    "attn_fwd_kernel": "paged_kv_block_amd/csrc/attn_fwd.hip",
+    "decode_coop_kernel": "paged_kv_block_amd/csrc/decode_fwd.hip",
+    "decode_kernel": "paged_kv_block_amd/csrc/decode_fwd.hip",
+    "decode_merge_kernel": "paged_kv_block_amd/csrc/decode_fwd.hip",
+    "sage_kernel": "paged_kv_block_amd/csrc/sage_fwd.hip",
+    "qsa_kernel": "paged_kv_block_amd/csrc/qsa_fwd.hip",
+}
+_COMMON_SOURCES = ["paged_kv_block_amd/csrc/device_common.h",
+                   "paged_kv_block_amd/csrc/pkb_internal.h", "paged_kv_block_amd/csrc/policy.h"]
+_TRAFFIC_WORKLOADS = {"decode": "decode", "decode_q": "decode_q", "bsa": "bsa",
+                      "prefill": "prefill_d128_w-1", "prefill_w1024": "prefill_d128_w1024",
+                      "prefill256": "prefill_d256_w-1", "sage": "sage", "qsa": "qsa"}
+
+
+def _short_kernel(name):
+    """'void pkb::attn_fwd_kernel<128, 4, 0, false, true>(...)' -> 'attn_fwd_kernel<128,4,bsa>'."""
+    import re
+    m = re.search(r"pkb::(\w+)(?:<([^>]*)>)?\(", name)
+    if not m:
+        return None
+    base, targs = m.group(1), [t.strip() for t in (m.group(2) or "").split(",") if t.strip()]
+    if base == "attn_fwd_kernel":
+        return f"attn_fwd_kernel<{targs[0]},{targs[1]},{['bsa', 'prefill', 'decode'][int(targs[2])]}>"
+    if base in ("decode_coop_kernel", "decode_kernel", "decode_merge_kernel", "qsa_kernel"):
+        return f"{base}<{targs[0]}>"
+    return base
+
+
+def _counter_means(path, last):
+    import csv
+    vals, durs = {}, {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            k = row["Kernel_Name"]
+            vals.setdefault(k, {}).setdefault(row["Counter_Name"], {})[int(row["Dispatch_Id"])] = \
+                float(row["Counter_Value"])
+    out = {}
+    for k, cs in vals.items():
+        for c, v in cs.items():
+            ids = sorted(v)[-last:]
+            out.setdefault(k, {})[c] = float(np.mean([v[i] for i in ids]))
+    return out
+
+
+def traffic_summary(directory, last=4):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE runs, one counter per run, in
+    <directory>/tf_<workload>_<COUNTER>/p_counter_collection.csv.  Each counter (KiB per
+    dispatch) is scaled by what it reads for the plain 1 GiB device copy (tf_copy_*: three
+    __amd_rocclr_copyBuffer launches of 1,048,576 KiB).  Prints the table rows and the
+    machine-readable records that measured_traffic() reads."""
+    def load(w, c):
+        return _counter_means(os.path.join(directory, f"tf_{w}_{c}", "p_counter_collection.csv"), last)
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy = [v[c] for k, v in load("copy", c).items() if k.startswith("__amd_rocclr_copyBuffer")]
+        cal[c] = (1 << 20) / copy[0]
+    rows = ["| calibration (1 GiB = 1,048,576 KiB copied) | counter reads (KiB) | scale factor |",
+            "|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows.append(f"| {c} | {(1 << 20) / cal[c]:,.1f} | {cal[c]:.4f} |")
+    rows += ["", "| workload | kernel | FETCH_SIZE KiB / dispatch | WRITE_SIZE KiB / dispatch | "
+                 "bytes per launch |", "|---|---|---|---|---|"]
+    recs = []
+    for w, wname in _TRAFFIC_WORKLOADS.items():
+        fe, wr = load(w, "FETCH_SIZE"), load(w, "WRITE_SIZE")
+        for k in fe:
+            short = _short_kernel(k)
+            if short is None or k not in wr:
+                continue
+            f_kib, w_kib = fe[k]["FETCH_SIZE"], wr[k]["WRITE_SIZE"]
+            nbytes = int(round((f_kib * cal["FETCH_SIZE"] + w_kib * cal["WRITE_SIZE"]) * 1024))
+            src = [_KERNEL_SOURCES[short.split("<")[0]]] + _COMMON_SOURCES
+            rows.append(f"| {wname} | `{short}` | {f_kib:,.0f} | {w_kib:,.0f} | {nbytes:,} |")
+            recs.append(f"traffic-record: kernel={short} workload={wname} source={','.join(src)} "
+                        f"sha256={_sha256([os.path.join(ROOT, x) for x in src])} "
+                        f"fetch_kib={f_kib:.1f} write_kib={w_kib:.1f} "
+                        f"fetch_scale={cal['FETCH_SIZE']:.4f} write_scale={cal['WRITE_SIZE']:.4f} "
+                        f"bytes_per_launch={nbytes}")
+    return "\n".join(rows + [""] + recs)
+
+
 # ---------------------------------------------------------------------------- main
 
 def main(argv=None):
@@ -919,7 +1003,13 @@ def main(argv=None):
     ap.add_argument("--pmc-summary", metavar="COUNTER_COLLECTION_CSV", default=None,
                     help="print a markdown summary of a rocprofv3 counter collection and exit "
                          "(means over the last 2*steps dispatches of each kernel)")
+    ap.add_argument("--traffic-summary", metavar="DIR", default=None,
+                    help="print HBM traffic rows and records from FETCH_SIZE / WRITE_SIZE "
+                         "runs under DIR (tf_<workload>_<counter>/) and exit")
     a = ap.parse_args(argv)
+    if a.traffic_summary:
+        print(traffic_summary(a.traffic_summary))
+        return 0
     if a.trace_summary:
         print(trace_summary(a.trace_summary, 2 * a.steps))
         return 0

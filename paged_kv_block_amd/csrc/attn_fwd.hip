@@ -116,18 +116,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// 16 bytes per lane from global src to LDS address lds_addr + 16 * lane
-// (global_load_lds_dwordx4; the LDS base is taken from M0, which needs one wait
-// state after the SALU write).  Written as inline assembly so the compiler does
-// not treat every later LDS read as depending on every copy in flight: the
-// kernel orders copies and reads itself with s_waitcnt vmcnt and barriers (both
-// ordered with volatile asm), and the data read here is never written.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_addr) : "m0");
-}
-// The same copy from the wave-uniform address base + byte offset off (the
-// scalar-base form: the 64-bit base sits in SGPRs, each lane adds 32 bits).
+// 16 bytes per lane from the wave-uniform address base + byte offset off to LDS
+// address lds_addr + 16 * lane (global_load_lds_dwordx4 in its scalar-base
+// form: the 64-bit base sits in SGPRs, each lane adds 32 bits; the LDS base is
+// taken from M0, which needs one wait state after the SALU write).  Written as
+// inline assembly so the compiler does not treat every later LDS read as
+// depending on every copy in flight: the kernel orders copies and reads itself
+// with s_waitcnt vmcnt and barriers (both ordered with volatile asm), and the
+// data read here is never written.
 __device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(off), "s"(base), "s"(lds_addr) : "m0");
