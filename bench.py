@@ -311,9 +311,9 @@ def prefill_admitted_pairs(case):
 
 # ---------------------------------------------------------------------------- workloads
 
-def bench_decode(steps, warmup, W, P):
+def bench_decode(steps, warmup, W, P, page_size=16):
     log("decode: generating inputs")
-    case = W.batch_decode()
+    case = W.batch_decode(page_size=page_size)
     sha = input_sha256(case.q, case.k, case.v, case.kv_indptr, case.kv_indices, case.seq_lens)
     B, Hq, D = case.q.shape
     Hkv, ps = case.k.shape[1], case.k.shape[2]
@@ -336,14 +336,15 @@ def bench_decode(steps, warmup, W, P):
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     ach = kv_bytes / (ms_launch * 1e-3) / 1e9
     cfg = {"workload": "batch paged decode B=64 Hq=32 Hkv=8 D=128 seq_lens~U[512,8192] "
-                       "page_size=16 bf16 (seed 2)",
+                       f"page_size={ps} bf16 (seed 2)",
            "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "page_size": ps,
            "sum_seq_len": int(case.seq_lens.sum()), "num_splits": S, "split_len": split_len,
            "kv_bytes_per_step": kv_bytes, "input_sha256": sha}
     kern = ["decode_coop_kernel<128>"] if S == 1 else ["decode_kernel<128>", "decode_merge_kernel<128>"]
     gather = PEAKS.get("hbm_gather_4k_GBps")
     roof = roofline("hbm", ach, "GB/s", HBM_PEAK_GBS, "hbm_read_GBps",
-                    measured_traffic(kern, "decode"), " + ".join(kern) + " (one step)",
+                    measured_traffic(kern, "decode" if ps == 16 else f"decode_ps{ps}"),
+                    " + ".join(kern) + " (one step)",
                     per_unit="4096 B of K+V per live token (Hkv=8, D=128, bf16)")
     if gather:
         roof["frac_of_measured_4k_gather"] = round(ach / gather, 4)
@@ -901,7 +902,7 @@ def pmc_summary(path, last, num_cus=256, xcds=8):
 # Kernel short names and the sources each one is built from (a traffic record
 # is valid only while these files are unchanged).
 _KERNEL_SOURCES = {
-    "attn_fwd_kernel": "paged_kv_block_amd/csrc/attn_fwd.hip",
+    "attn_fwd_kernel": "paged_kv_block_amd/csrc/attn_fwd_kernel.h",
     "decode_coop_kernel": "paged_kv_block_amd/csrc/decode_fwd.hip",
     "decode_kernel": "paged_kv_block_amd/csrc/decode_fwd.hip",
     "decode_merge_kernel": "paged_kv_block_amd/csrc/decode_fwd.hip",
@@ -999,6 +1000,9 @@ def main(argv=None):
                     default=None,
                     help="run one workload only (for profiling; copy = counter calibration, "
                          "peaks = the on-device ceilings)")
+    ap.add_argument("--decode-page-size", type=int, default=16,
+                    help="page size of the decode batch (with --only decode; the headline "
+                         "uses 16)")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV", default=None,
                     help="print a markdown summary of a rocprofv3 kernel trace and exit (mean "
                          "over the last 2*steps dispatches of each kernel: the timed ones)")
@@ -1018,6 +1022,9 @@ def main(argv=None):
     if a.pmc_summary:
         print(pmc_summary(a.pmc_summary, 2 * a.steps))
         return 0
+    if a.decode_page_size != 16 and a.only != "decode":
+        print("--decode-page-size applies to --only decode", file=sys.stderr)
+        return 2
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU component "
               "(run with --gpus 1)", file=sys.stderr)
@@ -1039,7 +1046,8 @@ def main(argv=None):
 
     if a.only:
         if a.only == "decode":
-            case, gbs, ms_step, cfg, roof = bench_decode(a.steps, a.warmup, W, P)
+            case, gbs, ms_step, cfg, roof = bench_decode(a.steps, a.warmup, W, P,
+                                                         a.decode_page_size)
             print(json.dumps({"metric": "decode KV-read GB/s", "value": round(gbs, 1),
                               "unit": "GB/s", "ms_per_step": round(ms_step, 4), "config": cfg,
                               "roofline": roof}), flush=True)

@@ -121,8 +121,9 @@ const char* pkb_last_hip_error(void);
 /* Static (capacity-only) arguments.  The page plans from static capacities and
  * binds live metadata only at run time.
  *   B, Sq, Hq, Hkv, D      q is [B, Sq, Hq, D]; Hq % Hkv == 0; D in {128, 256}.
- *   num_pages, page_size   K/V pools [num_pages, Hkv, page_size, D];
- *                          page_size a positive multiple of 8.
+ *   num_pages, page_size   K/V pools [num_pages, Hkv, page_size, D]; page_size >= 1
+ *                          (multiples of 8 take the fastest copy path; others copy
+ *                          K/V row by row, since 8 tokens may then span pages).
  *   q_block_size           query tokens per BSR row; (q_block_size*Hq/Hkv) % 8 == 0.
  *   kv_block_size          KV tokens per logical block: 8, 16, 32 or a multiple of 64.
  *   max_seq_len_kv         static maximum live KV length, 1..PKB_MAX_SEQ_LEN.
@@ -282,7 +283,9 @@ int paged_prefill_run(const pkb_prefill_plan_t* plan, const int32_t* worklist_d,
 /* (page "prims_ts_batch_decode_with_kv_cache": description, Parameters)      */
 /* ======================================================================== */
 
-/* Static policy from max_seq_len (the page selects its policy from the static
+/* Any page_size >= 1 is accepted (sizes that are not a multiple of 8 translate
+ * every token's page on its own).
+ * Static policy from max_seq_len (the page selects its policy from the static
  * maximum): each request's keys are cut into chunks of split_len tokens (at
  * most num_splits chunks); workspace bytes paged_decode_run needs (0 when one
  * chunk suffices): fp32 partials [B, Hq, num_splits, D+4] (O, running max,

@@ -20,8 +20,9 @@ Metadata contracts come from the FlashInfer pages:
 
 Readings where the pages are silent (offsets are absolute into the flat index
 array; duplicate block IDs in a row are rejected; kv_indptr increases strictly
-as on the decode page; page_size must be a multiple of 8) are the ones the
-library documents in its header.
+as on the decode page) are the ones the library documents in its header.  The
+block-sparse and decode pages constrain only block sizes, so any page size of
+at least 1 is accepted there; the prefill page lists its four.
 """
 from __future__ import annotations
 
@@ -100,7 +101,7 @@ def bsa_plan(B, Sq, Hq, Hkv, D, num_pages, page_size, q_block_size, kv_block_siz
         return PKB_ERR_SHAPE, None
     if qkv_dtype != BF16 or out_dtype not in (BF16, FP32):
         return PKB_ERR_DTYPE, None
-    if D not in (128, 256) or page_size % 8:
+    if D not in (128, 256):
         return PKB_ERR_UNSUPPORTED, None
     G = Hq // Hkv
     if (q_block_size * G) % 8:
@@ -305,7 +306,7 @@ def decode_policy(B, Hq, Hkv, D, max_seq_len, page_size, num_cus, per_wave=8, ma
         return PKB_ERR_ARG, 0, 0, 0
     if Hq % Hkv:
         return PKB_ERR_SHAPE, 0, 0, 0
-    if D not in (128, 256) or page_size % 8:
+    if D not in (128, 256):
         return PKB_ERR_UNSUPPORTED, 0, 0, 0
     if not (1 <= max_seq_len <= MAX_SEQ_LEN):
         return PKB_ERR_ARG, 0, 0, 0

@@ -27,12 +27,14 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include")]
 
-HIP_SOURCES = ["attn_fwd.hip", "decode_fwd.hip", "sage_fwd.hip", "qsa_fwd.hip", "api.cpp"]
+HIP_SOURCES = ["attn_fwd.hip", "attn_ragged.hip", "decode_fwd.hip", "sage_fwd.hip", "qsa_fwd.hip",
+               "api.cpp"]
 # Per-source extra device flags.  The decode kernel fits in the 256 architectural
 # VGPRs, so its MFMA operands and accumulators are kept there: VALU work on the
 # accumulators (rescale, epilogue) then needs no AGPR <-> VGPR copies.
 SOURCE_FLAGS = {"decode_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "attn_ragged.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "qsa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 CPP_SOURCES = ["host.cpp"]
 PEAKS_SOURCES = ["peaks.hip"]

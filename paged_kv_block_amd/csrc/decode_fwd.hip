@@ -69,7 +69,10 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // of column qn), m_run the column's running max in scale * log2(e) units (-inf
 // when no key was admitted) and l_run this lane's share of the column's sum of
 // probabilities (quad_sum adds the four shares).  vs is the wave's V slab.
-template <int D, bool F32>
+// RAGGED: the page size is not a multiple of 8, so an 8-token chunk may span
+// pages and every token is translated on its own (lanes 0..31 hold the 32
+// tokens of a group; the loads fetch their row offsets with a lane shuffle).
+template <int D, bool F32, bool RAGGED>
 __device__ __forceinline__ void decode_part(const DecodeParams& p, int b, int kvh, int L, int qlen,
                                             int tok0, int r_lo, int r_hi, unsigned char* vs,
                                             f32x4 (&oacc)[D / 16], float& m_run, float& l_run) {
@@ -123,14 +126,14 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, int b, int kv
   // loads issued after it.  Every lane loads (the index is clamped into the
   // request's live range), so no path skips a load.
   auto page_id = [&](int grp) -> int {
-    const int t = min(t_base + grp * 32 + 8 * (lane & 3), L - 1);
+    const int t = min(t_base + grp * 32 + (RAGGED ? (lane & 31) : 8 * (lane & 3)), L - 1);
     return ids[t / p.page_size];
   };
-  // element offset of the chunk from its page ID; dead chunks get offset 0
-  // (page 0, always in bounds) and their keys are masked
+  // element offset of the chunk (RAGGED: the token) from its page ID; dead
+  // chunks get offset 0 (page 0, always in bounds) and their keys are masked
   auto chunk_off = [&](int grp, int id) -> int64_t {
-    const int t = t_base + grp * 32 + 8 * (lane & 3);
-    if (!(lane < 4 && grp < n_groups && t < L)) return 0;
+    const int t = t_base + grp * 32 + (RAGGED ? (lane & 31) : 8 * (lane & 3));
+    if (!((RAGGED || lane < 4) && grp < n_groups && t < L)) return 0;
     const int pi = t / p.page_size;
     return (int64_t)id * p.kv_page_stride + head_off + (int64_t)(t - pi * p.page_size) * D;
   };
@@ -141,6 +144,28 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, int b, int kv
   // V pieces are row-major (piece lane + 64i is key 4i + lane/16 at D = 128,
   // 2i + lane/32 at D = 256, so each load's chunk is wave-uniform).
   auto load_group = [&](int64_t off_v, bf16x8 (&ka)[2][KS], u32x4 (&vr)[VP]) {
+    if (RAGGED) {
+      // row offset of key k of the group, held by lane k
+      auto row_off = [&](int k) -> int64_t {
+        const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)off_v, k);
+        const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)((uint64_t)off_v >> 32), k);
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+      };
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t off = row_off(16 * u + qn) * 2 + 16 * g;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ka[u][s] = as_bf16x8(ld_global_16(kbase + off + 64 * s));
+      }
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const int piece = lane + 64 * i;
+        const int key = piece / (D / 8);
+        const int dp = piece - key * (D / 8);
+        vr[i] = ld_global_16(vbase + row_off(key) * 2 + dp * 16);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int64_t o0 = readlane_i64(off_v, 2 * u), o1 = readlane_i64(off_v, 2 * u + 1);
@@ -320,7 +345,7 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int64_t orow, i
   if (p.lse && write_lse) p.lse[orow] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
 }
 
-template <int D, bool F32>
+template <int D, bool F32, bool RAGGED>
 __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
   constexpr int DB = D / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -386,7 +411,8 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
 
     f32x4 oacc[DB];
     float m_run, l_run;
-    decode_part<D, F32>(p, b, kvh, L, qlen, tok0, c * CH, (c + 1) * CH, smem, oacc, m_run, l_run);
+    decode_part<D, F32, RAGGED>(p, b, kvh, L, qlen, tok0, c * CH, (c + 1) * CH, smem, oacc, m_run,
+                                l_run);
 
     // ---- item result: lane (qn, g) holds O^T rows 16d + 4g + i of head qn ----
     const float l_tot = quad_sum(l_run);
@@ -423,7 +449,7 @@ __global__ void __launch_bounds__(64) decode_kernel(const DecodeParams p) {
 // counterpart of longest-processing-time-first scheduling.  The waves of a
 // workgroup split an item's groups evenly, and their partial (O, m, l) are
 // merged through LDS into the final output: no workspace, no merge launch.
-template <int D, bool F32>
+template <int D, bool F32, bool RAGGED>
 __global__ void __launch_bounds__(kCoopWaves * 64) decode_coop_kernel(const DecodeParams p) {
   using Lay = DecLayout<D>;
   constexpr int DB = D / 16;
@@ -486,7 +512,7 @@ __global__ void __launch_bounds__(kCoopWaves * 64) decode_coop_kernel(const Deco
 
     f32x4 oacc[DB];
     float m_run, l_run;
-    decode_part<D, F32>(p, b, kvh, L, qlen, tok0, r_lo, r_hi, slab, oacc, m_run, l_run);
+    decode_part<D, F32, RAGGED>(p, b, kvh, L, qlen, tok0, r_lo, r_hi, slab, oacc, m_run, l_run);
     const float l_tot = quad_sum(l_run);
 
     // ---- merge of the waves' partials through LDS (the V slabs are free now) ----
@@ -653,25 +679,32 @@ template <int D>
 static hipError_t launch_dec(const DecodeParams& p, int grid, hipStream_t st) {
   DecodeParams arg = p;
   void* args[] = {(void*)&arg};
-  const void* kern = p.out_f32 ? (const void*)decode_kernel<D, true> : (const void*)decode_kernel<D, false>;
+  const bool ragged = (p.page_size & 7) != 0;
+  const void* kern = ragged ? (p.out_f32 ? (const void*)decode_kernel<D, true, true>
+                                         : (const void*)decode_kernel<D, false, true>)
+                            : (p.out_f32 ? (const void*)decode_kernel<D, true, false>
+                                         : (const void*)decode_kernel<D, false, false>);
   return hipLaunchKernel(kern, dim3(grid), dim3(64), args, DecLayout<D>::LDS, st);
 }
 
 template <int D>
 static hipError_t launch_coop(const DecodeParams& p, int grid, hipStream_t st) {
   const size_t lds = kCoopWaves * DecLayout<D>::LDS + 2 * kCoopMaxBatch * sizeof(int);
-  const void* kern = p.out_f32 ? (const void*)decode_coop_kernel<D, true>
-                               : (const void*)decode_coop_kernel<D, false>;
+  const bool ragged = (p.page_size & 7) != 0;
+  const void* kern = ragged ? (p.out_f32 ? (const void*)decode_coop_kernel<D, true, true>
+                                         : (const void*)decode_coop_kernel<D, false, true>)
+                            : (p.out_f32 ? (const void*)decode_coop_kernel<D, true, false>
+                                         : (const void*)decode_coop_kernel<D, false, false>);
   if (lds > 65536) {
     // The LDS limit is an attribute of the function on one device: raise it on
     // the first launch there only, so later launches (and graph capture) make
     // no extra runtime calls.
-    static std::atomic<uint64_t> raised[2];
+    static std::atomic<uint64_t> raised[4];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
-    std::atomic<uint64_t>& flag = raised[p.out_f32 ? 1 : 0];
+    std::atomic<uint64_t>& flag = raised[(p.out_f32 ? 1 : 0) + (ragged ? 2 : 0)];
     if (!(flag.load(std::memory_order_acquire) & bit)) {
       e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;

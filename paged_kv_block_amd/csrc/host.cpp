@@ -103,7 +103,7 @@ int bsa_plan(const bsa_static_args* a, bsa_plan_t* plan) {
   if (a->Hq % a->Hkv) return PKB_ERR_SHAPE;
   if (a->qkv_dtype != PKB_BF16 || (a->out_dtype != PKB_BF16 && a->out_dtype != PKB_FP32))
     return PKB_ERR_DTYPE;
-  if ((a->D != 128 && a->D != 256) || a->page_size % 8) return PKB_ERR_UNSUPPORTED;
+  if (a->D != 128 && a->D != 256) return PKB_ERR_UNSUPPORTED;
   const int G = a->Hq / a->Hkv;
   if (((int64_t)a->q_block_size * G) % 8) return PKB_ERR_ARG;
   const int kvbs = a->kv_block_size;
@@ -323,7 +323,7 @@ static int decode_split(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t m
                         size_t* bytes, int32_t* num_splits, int32_t* split_len) {
   if (B < 1 || Hq < 1 || Hkv < 1 || num_cus < 1 || page_size < 1) return PKB_ERR_ARG;
   if (Hq % Hkv) return PKB_ERR_SHAPE;
-  if ((D != 128 && D != 256) || page_size % 8) return PKB_ERR_UNSUPPORTED;
+  if (D != 128 && D != 256) return PKB_ERR_UNSUPPORTED;
   if (max_seq_len < 1 || max_seq_len > PKB_MAX_SEQ_LEN) return PKB_ERR_ARG;
   if (pkb::decode_coop(B, Hkv, (int)std::min<int64_t>((int64_t)max_q * (Hq / Hkv), 1 << 30), num_cus)) {
     if (num_splits) *num_splits = 1;

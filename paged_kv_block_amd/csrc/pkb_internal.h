@@ -117,6 +117,9 @@ struct QsaParams {
 
 hipError_t launch_attn(const AttnParams& p, int D, int waves, int mode, dim3 grid,
                        hipStream_t stream);
+// page sizes that are not a multiple of 8 (launch_attn forwards them here)
+hipError_t launch_attn_ragged(const AttnParams& p, int D, int waves, int mode, dim3 grid,
+                              hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int D, int grid, hipStream_t stream);
 hipError_t launch_decode_coop(const DecodeParams& p, int D, int grid, hipStream_t stream);
 hipError_t launch_decode_merge(const MergeParams& p, int D, hipStream_t stream);

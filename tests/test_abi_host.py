@@ -202,6 +202,38 @@ def test_window_requires_causal_and_static_rules():
     assert _c_bsa_plan(dict(base, Hq=3, Hkv=2))[0] == M.PKB_ERR_SHAPE
 
 
+def test_small_page_quotient_rule():
+    """The attention kernel finds a row's page inside a chunk from the slot x
+    of the chunk's first token plus the row (x < page_size + 7): for page sizes
+    below 8 as (x * ceil(2^32 / page_size)) >> 32, else as x >= page_size.
+    Both equal x // page_size over every operand they receive."""
+    for ps in range(1, 8):
+        magic = ((1 << 32) + ps - 1) // ps
+        assert all((x * magic) >> 32 == x // ps for x in range(ps + 7))
+    for ps in list(range(8, 600)) + [4095, 65536, 1 << 20]:
+        assert all(int(x >= ps) == x // ps for x in range(ps + 7))
+
+
+def test_any_page_size_for_block_sparse_and_decode():
+    """The block-sparse and decode pages constrain block sizes only, so every
+    page size >= 1 plans (prefill keeps its page's four sizes)."""
+    base = dict(B=1, Sq=16, Hq=4, Hkv=1, D=128, num_pages=4, page_size=16, q_block_size=16,
+                kv_block_size=32, max_seq_len_kv=64, mask_type=0, window_left=-1, qkv_dtype=0,
+                out_dtype=0, num_cus=256)
+    for ps in (1, 2, 3, 5, 7, 12, 17, 20, 24, 100):
+        assert _c_bsa_plan(dict(base, page_size=ps))[0] == 0, ps
+        assert P.paged_decode_workspace_size(4, 32, 8, 128, 1000, ps, 256)[1] >= 1
+        assert P.paged_decode_q_workspace_size(4, 3, 32, 8, 128, 1000, ps, 256)[1] >= 1
+    assert _c_bsa_plan(dict(base, page_size=0))[0] == M.PKB_ERR_ARG
+    with pytest.raises(P.PkbError):
+        P.paged_decode_workspace_size(4, 32, 8, 128, 1000, 0, 256)
+    for ps in (8, 24, 48):
+        st = C.lib().paged_prefill_validate(
+            ctypes.byref(C.PrefillStaticArgs(1, 4, 1, 128, 4, ps, 16, 4, 1, -1, 0, 0, 256)),
+            None, None, None, 0, ctypes.byref(C.Bad()))
+        assert st == M.PKB_ERR_UNSUPPORTED, ps
+
+
 # ----------------------------------------------------------------------------- prefill
 
 def _prefill_args(B, total_q, width, mask_type=1, window_left=-1, page_size=32, D=128, Hq=32,
