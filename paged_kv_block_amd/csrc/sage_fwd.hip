@@ -272,39 +272,46 @@ sage_kernel(const SageParams p) {
       float mx = -INFINITY;
       int kvh = kv - 32 * hh;        // keys of this lane half below the block size
       if (p.causal) kvh = min(kvh, p_row - bm[0].beta * 64 - 32 * hh + 1);
-      // sv * scl is the scaled score.  Blocks that no row of the wave cuts keep
-      // raw scores (scl = sc) and scale only their row max, |sc| times the max
-      // of sign(sc) * score, exact since scaling keeps or reverses the order;
-      // the scale then rides in the exponent's FMA.
-      float scl = 1.f;
+      // sv * scl is the scaled score: the raw scores (scl = sc), with keys at
+      // or past the block end (or the causal edge) replaced in place by a value
+      // whose product with sc is -inf, so both paths leave the scores in the
+      // same registers.  The row max is taken on the raw scores, |sc| times the
+      // max of sign(sc) * score, exact since scaling keeps or reverses the
+      // order; the scale then rides in the exponent's FMA.  A zero scale
+      // (all-zero quantised block) takes the explicit path.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[kb][i] = (float)sacc[kb][i];
+      float scl = sc;
       if (__builtin_amdgcn_ballot_w64(kvh < 32)) {
+        if (sc != 0.f) {
+          const float dead = sc > 0.f ? -INFINITY : INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[kb][i] = (16 * kb + i < kvh) ? sv[kb][i] : dead;
+        } else {
+          // every live score is 0
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[kb][i] = (16 * kb + i < kvh) ? 0.f : -INFINITY;
+          scl = 1.f;
+        }
+      }
+      if (scl >= 0.f) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float x = (16 * kb + i < kvh) ? (float)sacc[kb][i] * sc : -INFINITY;
-            sv[kb][i] = x;
-            mx = fmaxf(mx, x);
-          }
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sv[kb][i] = (float)sacc[kb][i];
-        if (sc >= 0.f) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sv[kb][i]);
-        }
-        mx *= fabsf(sc);
-        scl = sc;
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sv[kb][i]);
       }
+      mx *= fabsf(scl);
       mx = half_max(mx);
       const float m_ref = (mx > m_run + kSlack) ? mx : m_run;
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
