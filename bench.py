@@ -177,7 +177,10 @@ def _peaks_lib():
     L.pkb_peak_hbm_gather.argtypes = [vp, i64, i64, vp, i32, ctypes.POINTER(i64), vp]
     L.pkb_peak_l2_gather.argtypes = [vp, i64, i64, vp, i32, ctypes.POINTER(i64), vp]
     L.pkb_peak_mfma.argtypes = [i32, i32, vp, i32, vp]
-    for f in (L.pkb_peak_hbm_read, L.pkb_peak_hbm_gather, L.pkb_peak_l2_gather, L.pkb_peak_mfma):
+    L.pkb_peak_issue.argtypes = [i32, i32, i32, vp, i32, vp]
+    L.pkb_peak_coexec.argtypes = [i32, i32, i32, vp, i32, vp]
+    for f in (L.pkb_peak_hbm_read, L.pkb_peak_hbm_gather, L.pkb_peak_l2_gather, L.pkb_peak_mfma,
+              L.pkb_peak_issue, L.pkb_peak_coexec):
         f.restype = ctypes.c_int
     return L
 
@@ -204,7 +207,8 @@ def measure_peaks(P):
     """Ceilings of this device from hand-written probe kernels: an HBM streaming
     read of 4 GiB, a gather of random 4 KiB slabs (decode's access shape), a
     gather of random 512-byte rows from a 2 MiB L2-resident buffer (the
-    packed-query kernel's), and dense MFMA loops at two waves per SIMD."""
+    packed-query kernel's), dense MFMA loops at two waves per SIMD, and the
+    instruction-issue and MFMA / VALU co-execution probes."""
     L = _peaks_lib()
     st = torch.cuda.current_stream().cuda_stream
     ncu = P.num_cus()
@@ -238,7 +242,24 @@ def measure_peaks(P):
     # Sage runs equal int8 (QK^T) and fp8 (PV) operation counts: its ceiling is
     # the harmonic mean of the two.
     out["mfma_i8_f8_half_TOPs"] = 2.0 / (1.0 / out["mfma_i8_TOPs"] + 1.0 / out["mfma_f8_TOPs"])
-    return {k: round(v, 1) for k, v in out.items()}
+    res = {k: round(v, 1) for k, v in out.items()}
+    # Issue rates (SIMD cycles per wave instruction at the 2.4 GHz the MFMA loop
+    # runs at) with one and two waves per SIMD, and MFMA / VALU co-execution.
+    clk = 2.4e9
+    iters = 20000
+    for kind, key in ((0, "fma"), (1, "exp"), (2, "add_and_salu")):
+        for waves in (4, 8):
+            ms = _best_ms(lambda: ok(L.pkb_peak_issue(kind, iters, waves, sink.data_ptr(), ncu, st),
+                                     "issue"))
+            res[f"issue_{key}_cycles_{waves // 4}wave"] = round(
+                ms * 1e-3 * clk / (iters * 8 * (waves // 4)), 2)
+    t = {}
+    for mode in (0, 1, 2):
+        t[mode] = _best_ms(lambda: ok(L.pkb_peak_coexec(mode, 10000, 40000, sink.data_ptr(), ncu, st),
+                                      "coexec"))
+    res["coexec_mfma_ms"], res["coexec_valu_ms"], res["coexec_both_ms"] = (
+        round(t[0], 4), round(t[1], 4), round(t[2], 4))
+    return res
 
 
 # ---------------------------------------------------------------------------- work counts

@@ -47,6 +47,24 @@ int pkb_peak_l2_gather(const void* buf, int64_t bytes, int64_t n_reads, void* si
  * 8 * (operations per instruction). */
 int pkb_peak_mfma(int32_t kind, int32_t iters, void* sink, int32_t grid, void* stream);
 
+/* Instruction-issue probe (512-thread workgroups holding 96 KB of LDS each, so
+ * one per CU; grid = number of CUs): in each
+ * workgroup the first `waves` waves (4 = one per SIMD, 8 = two per SIMD) run
+ * `iters` rounds of 8 independent instructions of one kind -- 0: v_fma_f32
+ * with three VGPR sources, 1: v_exp_f32, 2: v_add_f32 each followed by an
+ * independent s_add_u32 -- and the rest exit.  SIMD cycles per instruction =
+ * duration x clock / (iters x 8 x waves / 4). */
+int pkb_peak_issue(int32_t kind, int32_t iters, int32_t waves, void* sink, int32_t grid,
+                   void* stream);
+
+/* MFMA / VALU co-execution probe (512-thread workgroups, one per CU as above): waves
+ * 0-3 run iters_m rounds of 4 independent v_mfma_f32_32x32x16_bf16 (mode 0
+ * and 2), waves 4-7 -- on the same four SIMDs -- iters_v rounds of 8
+ * independent v_fma_f32 (mode 1 and 2).  Mode 2's duration against modes 0
+ * and 1 shows how far the two overlap. */
+int pkb_peak_coexec(int32_t mode, int32_t iters_m, int32_t iters_v, void* sink, int32_t grid,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

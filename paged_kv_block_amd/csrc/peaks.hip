@@ -4,6 +4,8 @@
 // loops in bf16, int8 and fp8.  Measurement code only.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "../../include/pkb_peaks.h"
 #include "device_common.h"
 
@@ -162,7 +164,107 @@ __global__ void __launch_bounds__(256) mfma_kernel(int iters, uint32_t* sink) {
   if (__float_as_uint(chk) == kMagic) sink[0] = kMagic;
 }
 
+// Vector-issue probe: every wave of the first `waves` of each 512-thread
+// workgroup runs `iters` rounds of 8 independent instructions of one kind
+// (0: v_fma_f32 with three VGPR sources, 1: v_exp_f32, 2: v_add_f32
+// interleaved with an independent s_add_u32); the other waves exit at once.
+// With one 512-thread workgroup per CU, waves w and w+4 share a SIMD, so
+// waves = 4 puts one wave on each SIMD and waves = 8 two.
+template <int KIND>
+__global__ void __launch_bounds__(512) issue_kernel(int iters, int waves, uint32_t* sink) {
+  const int t = threadIdx.x;
+  if (__builtin_amdgcn_readfirstlane(t >> 6) >= waves) return;
+  float x0 = t, x1 = t + 1, x2 = t + 2, x3 = t + 3, x4 = t + 4, x5 = t + 5, x6 = t + 6, x7 = t + 7;
+  const float c1 = 0.999f + t * 1e-9f, c2 = 0.001f + t * 1e-9f;
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (KIND == 0)
+      asm volatile(
+          "v_fma_f32 %0, %0, %8, %9\n\tv_fma_f32 %1, %1, %8, %9\n\tv_fma_f32 %2, %2, %8, %9\n\t"
+          "v_fma_f32 %3, %3, %8, %9\n\tv_fma_f32 %4, %4, %8, %9\n\tv_fma_f32 %5, %5, %8, %9\n\t"
+          "v_fma_f32 %6, %6, %8, %9\n\tv_fma_f32 %7, %7, %8, %9"
+          : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3), "+v"(x4), "+v"(x5), "+v"(x6), "+v"(x7)
+          : "v"(c1), "v"(c2));
+    else if constexpr (KIND == 1)
+      asm volatile(
+          "v_exp_f32 %0, %0\n\tv_exp_f32 %1, %1\n\tv_exp_f32 %2, %2\n\tv_exp_f32 %3, %3\n\t"
+          "v_exp_f32 %4, %4\n\tv_exp_f32 %5, %5\n\tv_exp_f32 %6, %6\n\tv_exp_f32 %7, %7"
+          : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3), "+v"(x4), "+v"(x5), "+v"(x6), "+v"(x7));
+    else
+      // (the scalar adds work on four SGPRs reserved through the clobber list)
+      asm volatile(
+          "v_add_f32 %0, %0, %8\n\ts_add_u32 s40, s40, 3\n\tv_add_f32 %1, %1, %8\n\ts_add_u32 s41, s41, 5\n\t"
+          "v_add_f32 %2, %2, %8\n\ts_add_u32 s42, s42, 7\n\tv_add_f32 %3, %3, %8\n\ts_add_u32 s43, s43, 9\n\t"
+          "v_add_f32 %4, %4, %8\n\ts_add_u32 s40, s40, 3\n\tv_add_f32 %5, %5, %8\n\ts_add_u32 s41, s41, 5\n\t"
+          "v_add_f32 %6, %6, %8\n\ts_add_u32 s42, s42, 7\n\tv_add_f32 %7, %7, %8\n\ts_add_u32 s43, s43, 9"
+          : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3), "+v"(x4), "+v"(x5), "+v"(x6), "+v"(x7)
+          : "v"(c1)
+          : "s40", "s41", "s42", "s43", "scc");
+  }
+  const float chk = x0 + x1 + x2 + x3 + x4 + x5 + x6 + x7;
+  if (__float_as_uint(chk) == kMagic) sink[0] = kMagic;
+}
+
+// Co-execution probe: waves 0-3 of each 512-thread workgroup run `iters_m`
+// rounds of 4 independent bf16 MFMAs (mode 0 or 2), waves 4-7 `iters_v`
+// rounds of 8 independent v_fma_f32 (mode 1 or 2).
+template <int MODE>
+__global__ void __launch_bounds__(512) coexec_kernel(int iters_m, int iters_v, uint32_t* sink) {
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  float chk = 0.f;
+  if (wave < 4) {
+    if (MODE == 1) return;
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (__bf16)(0.001f * (float)((t + i) & 7));
+      b[i] = (__bf16)(0.002f * (float)((t * 3 + i) & 7));
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
+    for (int it = 0; it < iters_m; ++it)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) chk += acc[c][0] + acc[c][15];
+  } else {
+    if (MODE == 0) return;
+    float x0 = t, x1 = t + 1, x2 = t + 2, x3 = t + 3, x4 = t + 4, x5 = t + 5, x6 = t + 6, x7 = t + 7;
+    const float c1 = 0.999f + t * 1e-9f, c2 = 0.001f + t * 1e-9f;
+    for (int it = 0; it < iters_v; ++it)
+      asm volatile(
+          "v_fma_f32 %0, %0, %8, %9\n\tv_fma_f32 %1, %1, %8, %9\n\tv_fma_f32 %2, %2, %8, %9\n\t"
+          "v_fma_f32 %3, %3, %8, %9\n\tv_fma_f32 %4, %4, %8, %9\n\tv_fma_f32 %5, %5, %8, %9\n\t"
+          "v_fma_f32 %6, %6, %8, %9\n\tv_fma_f32 %7, %7, %8, %9"
+          : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3), "+v"(x4), "+v"(x5), "+v"(x6), "+v"(x7)
+          : "v"(c1), "v"(c2));
+    chk = x0 + x1 + x2 + x3 + x4 + x5 + x6 + x7;
+  }
+  if (__float_as_uint(chk) == kMagic) sink[0] = kMagic;
+}
+
 inline int status(hipError_t e) { return e == hipSuccess ? 0 : -(int)e; }
+
+// The issue and co-execution probes reserve 96 KB of LDS (unused) so that at
+// most one of their 512-thread workgroups runs on a CU: waves w and w+4 then
+// share a SIMD.
+constexpr int kProbeLds = 96 * 1024;
+template <auto KERN>
+hipError_t allow_probe_lds() {
+  // once per kernel and device
+  static std::atomic<uint64_t> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, kProbeLds);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 }  // namespace
 
@@ -212,6 +314,46 @@ int pkb_peak_mfma(int32_t kind, int32_t iters, void* sink, int32_t grid, void* s
   else if (kind == 1) mfma_kernel<1><<<grid, 256, 0, s>>>(iters, (uint32_t*)sink);
   else if (kind == 2) mfma_kernel<2><<<grid, 256, 0, s>>>(iters, (uint32_t*)sink);
   else return -(int)hipErrorInvalidValue;
+  return status(hipGetLastError());
+}
+
+int pkb_peak_issue(int32_t kind, int32_t iters, int32_t waves, void* sink, int32_t grid,
+                   void* stream) {
+  if (!sink || iters < 1 || waves < 1 || waves > 8 || grid < 1) return -(int)hipErrorInvalidValue;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (kind == 0) {
+    if ((e = allow_probe_lds<issue_kernel<0>>()) != hipSuccess) return status(e);
+    issue_kernel<0><<<grid, 512, kProbeLds, s>>>(iters, waves, (uint32_t*)sink);
+  } else if (kind == 1) {
+    if ((e = allow_probe_lds<issue_kernel<1>>()) != hipSuccess) return status(e);
+    issue_kernel<1><<<grid, 512, kProbeLds, s>>>(iters, waves, (uint32_t*)sink);
+  } else if (kind == 2) {
+    if ((e = allow_probe_lds<issue_kernel<2>>()) != hipSuccess) return status(e);
+    issue_kernel<2><<<grid, 512, kProbeLds, s>>>(iters, waves, (uint32_t*)sink);
+  } else {
+    return -(int)hipErrorInvalidValue;
+  }
+  return status(hipGetLastError());
+}
+
+int pkb_peak_coexec(int32_t mode, int32_t iters_m, int32_t iters_v, void* sink, int32_t grid,
+                    void* stream) {
+  if (!sink || iters_m < 1 || iters_v < 1 || grid < 1) return -(int)hipErrorInvalidValue;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (mode == 0) {
+    if ((e = allow_probe_lds<coexec_kernel<0>>()) != hipSuccess) return status(e);
+    coexec_kernel<0><<<grid, 512, kProbeLds, s>>>(iters_m, iters_v, (uint32_t*)sink);
+  } else if (mode == 1) {
+    if ((e = allow_probe_lds<coexec_kernel<1>>()) != hipSuccess) return status(e);
+    coexec_kernel<1><<<grid, 512, kProbeLds, s>>>(iters_m, iters_v, (uint32_t*)sink);
+  } else if (mode == 2) {
+    if ((e = allow_probe_lds<coexec_kernel<2>>()) != hipSuccess) return status(e);
+    coexec_kernel<2><<<grid, 512, kProbeLds, s>>>(iters_m, iters_v, (uint32_t*)sink);
+  } else {
+    return -(int)hipErrorInvalidValue;
+  }
   return status(hipGetLastError());
 }
 

@@ -46,8 +46,8 @@ def test_peaks_library_exports_its_header():
     """libpkb_peaks.so (the on-device ceilings the benchmark measures) exports
     every function include/pkb_peaks.h declares."""
     names = header_functions("pkb_peaks.h")
-    assert names == ["pkb_peak_hbm_gather", "pkb_peak_hbm_read", "pkb_peak_l2_gather",
-                     "pkb_peak_mfma"]
+    assert names == ["pkb_peak_coexec", "pkb_peak_hbm_gather", "pkb_peak_hbm_read",
+                     "pkb_peak_issue", "pkb_peak_l2_gather", "pkb_peak_mfma"]
     lib = os.path.join(ROOT, "paged_kv_block_amd", "libpkb_peaks.so")
     out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True,
                          check=True).stdout
