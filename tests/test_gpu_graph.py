@@ -199,6 +199,58 @@ def test_graph_decode_replays(Hq, Hkv):
         assert_close(f64(gl), ref_l, TOL_LSE, f"lse replay {r}")
 
 
+# Single-pass decode (a wide batch for the given num_cus) and the allocation-free
+# entry point (its split partials in the library's fixed scratch) under capture.
+@pytest.mark.parametrize("entry,ncu", [("run", 4), ("noalloc", 4), ("noalloc", 256)])
+def test_graph_decode_single_pass_and_noalloc_replays(entry, ncu):
+    B, Hq, Hkv, D, ps, maxlen = 6, 32, 8, 128, 16, 3000
+    lens = [[1, 3000, 70, 900, 33, 2048], [2999, 5, 1200, 64, 640, 1],
+            [640, 641, 1, 2048, 3000, 17], [3000] * 6]
+    cases = [W.make_decode(990 + r, B, Hq, Hkv, D, L, ps, extra_pages=r, max_seq_len=maxlen)
+             for r, L in enumerate(lens)]
+    _, S, _ = P.paged_decode_workspace_size(B, Hq, Hkv, D, maxlen, ps, ncu)
+    assert (S == 1) == (ncu == 4)
+    Pcap = _pool(cases, "k")
+    k = torch.zeros(Pcap, Hkv, ps, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    q = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=DEV)
+    ip = torch.empty(B + 1, dtype=torch.int32, device=DEV)
+    ix = torch.zeros(max(c.kv_indices.size for c in cases), dtype=torch.int32, device=DEV)
+    sl = torch.empty(B, dtype=torch.int32, device=DEV)
+    nbytes, _, _ = P.paged_decode_workspace_size(B, Hq, Hkv, D, maxlen, ps, ncu)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+
+    def stage(c):
+        for dst, src in ((q, c.q), (k, c.k), (v, c.v), (ip, c.kv_indptr), (ix, c.kv_indices),
+                         (sl, c.seq_lens)):
+            _stage(dst, src)
+
+    def run(o=out, l=lse):
+        if entry == "run":
+            P.paged_decode_run(q, (k, v), ip, ix, sl, maxlen, ws, out=o, lse=l, num_cus_=ncu)
+        else:
+            P.paged_decode_run_noalloc(q, (k, v), ip, ix, sl, maxlen, out=o, lse=l, num_cus_=ncu)
+
+    stage(cases[0])
+    g = _capture(run)
+    for r in range(REPLAYS):
+        c = cases[r % len(cases)]
+        _say("decode graph replay", entry, ncu, r, c.seq_lens.tolist(), "splits", S)
+        stage(c)
+        g.replay()
+        torch.cuda.synchronize()
+        go, gl = out.clone(), lse.clone()
+        eo, el = torch.empty_like(out), torch.empty_like(lse)
+        run(eo, el)
+        torch.cuda.synchronize()
+        assert torch.equal(go, eo) and torch.equal(gl, el), f"replay {r} differs from eager"
+        ref_o, ref_l = oracle_decode(c)
+        assert_close(f64(go), ref_o, TOL_BF16, f"out replay {r}")
+        assert_close(f64(gl), ref_l, TOL_LSE, f"lse replay {r}")
+
+
 @pytest.mark.parametrize("max_q", [6, 4])     # 6 x 4 heads: general kernel; 4 x 4: decode kernel
 def test_graph_decode_q_packed_replays(max_q):
     B, Hq, Hkv, D, ps, maxlen, total_cap = 3, 32, 8, 128, 16, 2000, 18
