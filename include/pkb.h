@@ -58,7 +58,10 @@
 extern "C" {
 #endif
 
-#define PKB_ABI_VERSION 2
+/* 3: a NaN softmax scale selects the default and other non-positive or
+ * non-finite scales are rejected; paged_decode_run_noalloc; any page size >= 1
+ * for block-sparse and decode pools. */
+#define PKB_ABI_VERSION 3
 
 /* Largest max_seq_len accepted: 2^31 - 128, so that a 128-token padded tile end
  * still fits in int32 (page "prims_ts_batch_decode_with_kv_cache", description of

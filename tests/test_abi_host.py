@@ -57,7 +57,7 @@ def test_peaks_library_exports_its_header():
 
 def test_status_strings_and_version():
     L = P.lib()
-    assert L.pkb_abi_version() == 2
+    assert L.pkb_abi_version() == 3
     for st in range(0, -8, -1):
         assert L.pkb_status_string(st).decode() not in ("", "unknown status")
     assert M.MAX_SEQ_LEN == 2147483520 == C.PKB_MAX_SEQ_LEN   # 2^31 - 128
