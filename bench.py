@@ -221,17 +221,27 @@ def measure_peaks(P):
         if rc != 0:
             raise RuntimeError(f"{what} failed (HIP error {-rc})")
 
-    ms = _best_ms(lambda: ok(L.pkb_peak_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), ncu * 8, st),
-                             "hbm read"))
-    out["hbm_read_GBps"] = nbytes / (ms * 1e-3) / 1e9
+    # each ceiling is the best over 4, 8, 16 and 32 waves per CU
+    best = 0.0
+    for mult in (1, 2, 4, 8):
+        ms = _best_ms(lambda: ok(L.pkb_peak_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                                     ncu * mult, st), "hbm read"))
+        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    out["hbm_read_GBps"] = best
     got = ctypes.c_int64(0)
-    ms = _best_ms(lambda: ok(L.pkb_peak_hbm_gather(buf.data_ptr(), nbytes, 1 << 20, sink.data_ptr(),
-                                                   ncu * 4, ctypes.byref(got), st), "hbm gather"))
-    out["hbm_gather_4k_GBps"] = got.value / (ms * 1e-3) / 1e9
+    best = 0.0
+    for mult in (1, 2, 4, 8):
+        ms = _best_ms(lambda: ok(L.pkb_peak_hbm_gather(buf.data_ptr(), nbytes, 1 << 20, sink.data_ptr(),
+                                                       ncu * mult, ctypes.byref(got), st), "hbm gather"))
+        best = max(best, got.value / (ms * 1e-3) / 1e9)
+    out["hbm_gather_4k_GBps"] = best
     small = 2 << 20
-    ms = _best_ms(lambda: ok(L.pkb_peak_l2_gather(buf.data_ptr(), small, 1 << 24, sink.data_ptr(),
-                                                  ncu * 4, ctypes.byref(got), st), "l2 gather"))
-    out["l2_gather_512_GBps"] = got.value / (ms * 1e-3) / 1e9
+    best = 0.0
+    for mult in (1, 2, 4, 8):
+        ms = _best_ms(lambda: ok(L.pkb_peak_l2_gather(buf.data_ptr(), small, 1 << 24, sink.data_ptr(),
+                                                      ncu * mult, ctypes.byref(got), st), "l2 gather"))
+        best = max(best, got.value / (ms * 1e-3) / 1e9)
+    out["l2_gather_512_GBps"] = best
     del buf
     torch.cuda.empty_cache()
     grid, iters = ncu * 2, 4096
