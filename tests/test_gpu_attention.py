@@ -305,6 +305,21 @@ def test_decode_single_pass_growing_scores():
     assert_close(f64(lse), ref_l, TOL_LSE, "lse")
 
 
+@pytest.mark.parametrize("mask,w", [("dense", -1), ("causal", 50000)])
+def test_decode_long_requests_many_splits(mask, w):
+    """Requests of 131,072 and 100,000 tokens: the split policy cuts them into
+    about a thousand chunks, so the merge combines that many partials per row."""
+    case = W.make_decode(590, 2, 32, 8, 128, [131072, 100000], 16, mask=mask, window_left=w)
+    _say("decode long requests", mask, w)
+    out, lse, S = run_decode(case)
+    assert S > 256
+    ref_o, ref_l = oracle_decode(case)
+    assert_close(f64(out), ref_o, TOL_BF16, f"out (splits={S})")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, _, _ = run_decode(case, out_dtype=torch.float32)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
+
+
 def test_batch_decode_sampled():
     case = W.batch_decode()
     _say("batch_decode: generated", int(case.seq_lens.sum()))
