@@ -204,6 +204,22 @@ def test_batch_prefill_sampled(D, w):
     assert_close(f64(lse[rows]), ref_l, TOL_LSE, "lse")
 
 
+@pytest.mark.parametrize("D,w", [(128, -1), (128, 4096), (256, -1)])
+def test_prefill_long_context_sampled(D, w):
+    """Two requests with 64k- and 40k-token prefixes (about a thousand KV tiles
+    per work item), causal; sampled rows against the oracle."""
+    case = W.make_prefill(610 + D + max(w, 0), 2, [1024, 700], [65536, 40000], 32, 8, D, 32,
+                          window_left=w)
+    _say("prefill long context", D, w)
+    out, lse = run_prefill(case)
+    T = int(case.qo_indptr[-1])
+    rows = [0, 1, 511, 1023, 1024, 1400, T - 1]
+    ref_o, ref_l = oracle_prefill(case, rows=rows)
+    assert_close(f64(out[rows]), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse[rows]), ref_l, TOL_LSE, "lse")
+    assert torch.isfinite(out.float()).all()
+
+
 # ----------------------------------------------------------------------------- decode
 
 DECODE_SWEEP = [
