@@ -487,6 +487,7 @@ int qsa_run(const void* q, const void* k, const void* v, const uint8_t* sel_bloc
   p.lse = lse;
   p.T = T;
   p.NB = NB;
+  p.sel16 = (NB % 16 == 0 && ((uintptr_t)sel_blocks & 15) == 0) ? 1 : 0;
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.G = Hq / Hkv;

@@ -112,6 +112,7 @@ struct QsaParams {
   float* out_f32;             // [T, Hq, D] or null
   float* lse;                 // [Hq, T] or null
   int T, NB, Hq, Hkv, G;
+  int sel16;                  // NB % 16 == 0 and sel 16-byte aligned: 16-byte bitmap loads
   float scale_log2;
 };
 

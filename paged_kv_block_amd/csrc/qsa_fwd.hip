@@ -90,23 +90,46 @@ qsa_kernel(const QsaParams p) {
   const uint8_t* selrow = p.sel + (int64_t)t * p.NB;
 
   // ---- selected-block list ----
-  // Candidates go kChunk at a time: lane l tests blocks cb + 16l .. cb + 16l + 15,
+  // Candidates go kChunk at a time from a 16-aligned start: lane l tests blocks
+  // cb + 16l .. cb + 16l + 15 (one 16-byte load of the bitmap row where the
+  // row allows it, else 16 byte loads), keeps those inside [nb_lo, nb_hi], and
   // a wave-wide prefix sum of the counts places the selected ones, in order,
   // into this wave's LDS list (16-bit offsets from cb).  Groups then read 8
   // list entries from LDS, which never waits on the K/V loads in flight.
   uint16_t* list = (uint16_t*)(smem + Lay::LDS);
-  int cb = nb_lo;          // first candidate of the current list
+  int cb = nb_lo & ~15;    // first candidate of the current list
   int n_list = 0;          // entries in the current list
   int taken = 0;           // entries already handed out
+  // 4 bits: which bytes of x are nonzero (bit 7 of each byte after the
+  // carry-free test, then the four bits gathered by one multiply)
+  auto nz_bytes = [](uint32_t x) -> uint32_t {
+    const uint32_t t = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+    return ((t >> 7) * 0x00204081u >> 21) & 0xFu;
+  };
   auto build = [&]() {
-    // 16 unconditional byte loads (index clamped into the range) all in flight
-    uint8_t x[16];
+    const int first = cb + 16 * lane;
+    uint32_t nz = 0;
+    if (p.sel16) {
+      // the row is 16-byte aligned and first is a multiple of 16: the load
+      // stays inside the row whenever first <= NB - 16
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (first <= p.NB - 16) w = *(const u32x4*)(selrow + first);
 #pragma unroll
-    for (int b = 0; b < 16; ++b) x[b] = selrow[min(cb + 16 * lane + b, nb_hi)];
-    int flags = 0;
+      for (int d = 0; d < 4; ++d) nz |= nz_bytes(w[d]) << (4 * d);
+    } else {
+      // 16 unconditional byte loads (index clamped into the row) all in flight
+      uint8_t x[16];
 #pragma unroll
-    for (int b = 0; b < 16; ++b)
-      if (cb + 16 * lane + b <= nb_hi && x[b] != 0) flags |= 1 << b;
+      for (int b = 0; b < 16; ++b) x[b] = selrow[min(first + b, p.NB - 1)];
+#pragma unroll
+      for (int b = 0; b < 16; ++b)
+        if (x[b] != 0) nz |= 1u << b;
+    }
+    // keep the candidates inside [nb_lo, nb_hi]
+    const int lo_cut = min(max(nb_lo - first, 0), 16);
+    const int hi_cut = min(max(nb_hi + 1 - first, 0), 16);
+    const int flags0 = (int)(nz & ((1u << hi_cut) - 1u) & ~((1u << lo_cut) - 1u));
+    int flags = flags0;
     const int cnt = __builtin_popcount(flags);
     int incl = cnt;
 #pragma unroll

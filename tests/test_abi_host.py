@@ -214,6 +214,25 @@ def test_small_page_quotient_rule():
         assert all(int(x >= ps) == x // ps for x in range(ps + 7))
 
 
+def test_nonzero_byte_rule():
+    """The packed-query kernel marks the nonzero bytes of a 32-bit word as
+    bit 7 of (((x & 0x7F7F7F7F) + 0x7F7F7F7F) | x) & 0x80808080 and gathers
+    them with one multiply; over every zero / nonzero byte pattern (nonzero
+    bytes drawn from 1..255, 0x7F, 0x80 and 0xFF) that equals byte != 0."""
+    rng = np.random.default_rng(3)
+
+    def rule(x):
+        t = (((x & 0x7F7F7F7F) + 0x7F7F7F7F) | x) & 0x80808080
+        return ((((t >> 7) * 0x00204081) & 0xFFFFFFFF) >> 21) & 0xF
+
+    for pattern in range(16):
+        for _ in range(200):
+            bs = [int(rng.choice([1, 0x7F, 0x80, 0xFF, rng.integers(1, 256)])) if pattern >> i & 1 else 0
+                  for i in range(4)]
+            x = bs[0] | bs[1] << 8 | bs[2] << 16 | bs[3] << 24
+            assert rule(x) == pattern, (hex(x), pattern)
+
+
 def test_any_page_size_for_block_sparse_and_decode():
     """The block-sparse and decode pages constrain block sizes only, so every
     page size >= 1 plans (prefill keeps its page's four sizes)."""

@@ -45,6 +45,11 @@ QSA_SWEEP = [
     ([129, 3, 64], 16, 4, 128, dict(n_sel=5, mode="dense")),
     ([500], 12, 1, 256, dict(p_sel=1.0, mode="causal")),       # every block: causal attention
     ([40, 40], 12, 1, 256, dict(p_sel=0.0, mode="causal", force_diag=False)),   # all rows empty
+    # block counts that are multiples of 16: one 16-byte bitmap load per lane
+    ([64, 64], 12, 1, 256, dict(p_sel=0.5, mode="causal")),
+    ([256, 128], 8, 1, 128, dict(p_sel=0.3, mode="causal", window=90)),
+    ([1024, 960], 12, 1, 256, dict(n_sel=40, mode="dense", junk_bits=0.05)),
+    ([4864], 12, 1, 256, dict(n_sel=48, mode="causal")),      # 1216 blocks: two candidate chunks
 ]
 
 
