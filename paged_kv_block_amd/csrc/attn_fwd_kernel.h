@@ -773,23 +773,33 @@ attn_fwd_kernel(const AttnParams p) {
     l_run += psum;
     m_run = m_ref;
   };
-  // (V fragments of dim block d+1 are read while block d's MFMAs run.)
+  // Dim blocks go in groups of four, key step outermost: the four MFMAs of one
+  // step write four different accumulators, so none waits for the previous
+  // one's result (a chain of dependent MFMAs runs the matrix pipe at about
+  // two thirds of its rate).  The V fragments of the next step are read while
+  // the current step's MFMAs run.
   auto compute_pv = [&](int slot) {
-    bf16x8 va[2][4];
+    constexpr int GD = NDB < 4 ? NDB : 4;   // dim blocks per group
+    constexpr int NST = (NDB / GD) * 4;     // (group, key step) pairs
+    bf16x8 va[2][GD];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) va[0][s] = v_frag(slot, 0, s);
+    for (int d = 0; d < GD; ++d) va[0][d] = v_frag(slot, d, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      if (d + 1 < NDB) {
+    for (int st = 0; st < NST; ++st) {
+      const int g = st >> 2, s = st & 3;
+      if (st + 1 < NST) {
+        const int g1 = (st + 1) >> 2, s1 = (st + 1) & 3;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) va[(d + 1) & 1][s] = v_frag(slot, d + 1, s);
+        for (int d = 0; d < GD; ++d) va[(st + 1) & 1][d] = v_frag(slot, g1 * GD + d, s1);
       }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d & 1][s], pb[s], oacc[d], 0, 0, 0);
-        if (F32)
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d & 1][s], pl[s], oacc[d], 0, 0, 0);
+      for (int d = 0; d < GD; ++d)
+        oacc[g * GD + d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st & 1][d], pb[s], oacc[g * GD + d], 0, 0, 0);
+      if (F32) {
+#pragma unroll
+        for (int d = 0; d < GD; ++d)
+          oacc[g * GD + d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st & 1][d], pl[s], oacc[g * GD + d], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
