@@ -123,16 +123,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // 16 bytes per lane from the wave-uniform address base + byte offset off to LDS
-// address lds_addr + 16 * lane (global_load_lds_dwordx4 in its scalar-base
-// form: the 64-bit base sits in SGPRs, each lane adds 32 bits; the LDS base is
-// taken from M0, which needs one wait state after the SALU write).  Written as
-// inline assembly so the compiler does not treat every later LDS read as
-// depending on every copy in flight: the kernel orders copies and reads itself
-// with s_waitcnt vmcnt and barriers (both ordered with volatile asm), and the
-// data read here is never written.
-__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(lds_addr) : "m0");
+// address lds_a + lds_b + 16 * lane (global_load_lds_dwordx4 in its
+// scalar-base form: the 64-bit base sits in SGPRs, each lane adds 32 bits; the
+// LDS base is taken from M0, written by one SALU add, which needs one wait
+// state before the copy).  Written as inline assembly so the compiler does not
+// treat every later LDS read as depending on every copy in flight: the kernel
+// orders copies and reads itself with s_waitcnt vmcnt and barriers (both
+// ordered with volatile asm), and the data read here is never written.
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds_a, uint32_t lds_b) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_a), "s"(lds_b) : "m0", "scc");
 }
 
 // The same copy from a per-lane 64-bit address (global_load_lds_dwordx4 with
@@ -378,6 +378,30 @@ attn_fwd_kernel(const AttnParams p) {
       const int jj = j & 63;
       if (jj == 0 && j > 0) load_desc(j);   // next 64 tiles (rare)
       const int t0 = readlane_i32(d_t0, jj);
+      if (t0 >= k_lo && t0 + 64 <= k_hi) {
+        // Interior tile (the common case): every key is inside [k_lo, k_hi)
+        // and below L, so no range cut and no copy redirection.  The token
+        // bounds cover the whole tile; they only decide whether the causal and
+        // window masks run, which is exact either way.
+        uint64_t M = ~0ull;
+        if (MODE == kModeBsa && p.valid_bits) {
+          const uint32_t w0 = (uint32_t)readlane_i32((int)d_w0, jj);
+          const uint32_t w1 = (uint32_t)readlane_i32((int)d_w1, jj);
+          M = (uint64_t)w0 | ((uint64_t)w1 << 32);
+        }
+        tm.M = M;
+        tm.t0 = t0;
+        tm.tmin = t0;
+        tm.tmax = t0 + 63;
+        const int tw = t0 + SPAN * wave;
+        const int64_t src = readlane_i64(d_src, jj);
+#pragma unroll
+        for (int lc = 0; lc < CPW; ++lc) {
+          tm.tsrc[lc] = tw + 8 * lc;
+          tm.src[lc] = src + (int64_t)(8 * lc) * D;
+        }
+        return tm;
+      }
       const int lo = min(max(k_lo - t0, 0), 64);
       const int hi = min(max(k_hi - t0, 0), 64);
       uint64_t M = (hi >= 64 ? ~0ull : ((1ull << hi) - 1ull)) & ~(lo >= 64 ? ~0ull : ((1ull << lo) - 1ull));
@@ -500,8 +524,8 @@ attn_fwd_kernel(const AttnParams p) {
     const int key = i * Lay::KPI + lane / Lay::LPK;
     const uint32_t row = (uint32_t)((key & 7) * D * 2);
     const int pp = lane % Lay::LPK;
-    lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst + i * 1024);
-    lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst + i * 1024);
+    lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst, i * 1024);
+    lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst, i * 1024);
   };
   // Copies of tile j when chunks may span pages.  Each instruction still
   // copies KPI whole rows (1 KB), but from a per-lane address.  Per chunk, the
@@ -570,8 +594,8 @@ attn_fwd_kernel(const AttnParams p) {
         const int r = key & 7;
         const int pp = lane % Lay::LPK;
         const uint32_t row = (t + r < L) ? (uint32_t)(r * D * 2) : 0u;
-        lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst + i * 1024);
-        lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst + i * 1024);
+        lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst, i * 1024);
+        lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst, i * 1024);
       }
     }
   };
