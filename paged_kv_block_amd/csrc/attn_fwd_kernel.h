@@ -515,8 +515,9 @@ attn_fwd_kernel(const AttnParams p) {
     for (int lc = 0; lc < CPW; ++lc) whole = whole && (tm.tsrc[lc] + 8 <= L);
     return whole;
   };
-  // instruction ii of the copies of a whole tile j (no row of it past L)
-  auto issue_whole = [&](const TM& tm, int j, int ii) {
+  // instruction ii of the copies of a whole tile j (no row of it past L): its
+  // K copy (part bit 0) and V copy (bit 1)
+  auto issue_whole = [&](const TM& tm, int j, int ii, int part = 3) {
     const uint32_t kst = lds_base + (j % Lay::NSK) * Lay::TILE_B;
     const uint32_t vst = lds_base + Lay::V_BASE + (j % Lay::NSV) * Lay::TILE_B;
     const int i = wave * IPW + ii;
@@ -524,8 +525,8 @@ attn_fwd_kernel(const AttnParams p) {
     const int key = i * Lay::KPI + lane / Lay::LPK;
     const uint32_t row = (uint32_t)((key & 7) * D * 2);
     const int pp = lane % Lay::LPK;
-    lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst, i * 1024);
-    lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst, i * 1024);
+    if (part & 1) lds_dma16_s(p.k + tm.src[lc], row + (uint32_t)((pp ^ (key & 15)) * 16), kst, i * 1024);
+    if (part & 2) lds_dma16_s(p.v + tm.src[lc], row + (uint32_t)(v_unswz(key, pp) * 16), vst, i * 1024);
   };
   // Copies of tile j when chunks may span pages.  Each instruction still
   // copies KPI whole rows (1 KB), but from a per-lane address.  Per chunk, the
@@ -680,7 +681,10 @@ attn_fwd_kernel(const AttnParams p) {
   // S^T for the tile whose K sits in ring slot `slot`
   // (K fragments are read kKPre k-steps ahead of their MFMAs.)
   // When `cp` is set, the copies of whole tile cj go out one instruction per
-  // k-step, in the shadow of the MFMAs (the slot they fill is not read here).
+  // k-step, in the shadow of the MFMAs (the slot they fill is not read here);
+  // K and V copies on different k-steps, so an MFMA separates any two (two
+  // copies in a row need a wait state between the first's read of M0 and the
+  // second's write).
   auto compute_s = [&](int slot, f32x16 (&acc)[2], const TM* cp, int cj) {
     constexpr int kKPre = 4;
 #pragma unroll
@@ -705,10 +709,16 @@ attn_fwd_kernel(const AttnParams p) {
         for (int kb = 0; kb < 2; ++kb) kr[s % kKPre][kb] = k_frag(slot, kb, s + kKPre);
       }
       if (cp) {
-        constexpr int per = (IPW + NKS - 1) / NKS;
+        if constexpr (2 * IPW <= NKS) {
+          // K copies on the first IPW k-steps, V copies on the next IPW
+          if (s < IPW) issue_whole(*cp, cj, s, 1);
+          else if (s < 2 * IPW) issue_whole(*cp, cj, s - IPW, 2);
+        } else {
+          constexpr int per = (IPW + NKS - 1) / NKS;
 #pragma unroll
-        for (int u = 0; u < per; ++u)
-          if (s * per + u < IPW) issue_whole(*cp, cj, s * per + u);
+          for (int u = 0; u < per; ++u)
+            if (s * per + u < IPW) issue_whole(*cp, cj, s * per + u);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -767,7 +777,6 @@ attn_fwd_kernel(const AttnParams p) {
     const float m_new = mx * sl2;
     m_ref = (m_new > m_run + kRescaleSlack) ? m_new : m_run;
     m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    psum = 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 w, wl4;
@@ -775,7 +784,7 @@ attn_fwd_kernel(const AttnParams p) {
       for (int t = 0; t < 4; ++t) {
         const float e0 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t], sl2, -m_use));
         const float e1 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t + 1], sl2, -m_use));
-        psum += e0 + e1;
+        psum = (s == 0 && t == 0) ? e0 + e1 : psum + (e0 + e1);   // (no add of a zero start)
         w[t] = cvt_pk_bf16(e0, e1);
         if (F32)
           wl4[t] = cvt_pk_bf16(e0 - __uint_as_float(w[t] << 16), e1 - __uint_as_float(w[t] & 0xFFFF0000u));
