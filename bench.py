@@ -173,8 +173,8 @@ def _peaks_lib():
         raise ImportError(f"{path} not found: build it with paged_kv_block_amd/build.py")
     L = ctypes.CDLL(path)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-    L.pkb_peak_hbm_read.argtypes = [vp, i64, vp, i32, vp]
-    L.pkb_peak_hbm_gather.argtypes = [vp, i64, i64, vp, i32, ctypes.POINTER(i64), vp]
+    L.pkb_peak_hbm_read.argtypes = [vp, i64, vp, i32, i32, vp]
+    L.pkb_peak_hbm_gather.argtypes = [vp, i64, i64, vp, i32, i32, ctypes.POINTER(i64), vp]
     L.pkb_peak_l2_gather.argtypes = [vp, i64, i64, vp, i32, ctypes.POINTER(i64), vp]
     L.pkb_peak_mfma.argtypes = [i32, i32, vp, i32, vp]
     L.pkb_peak_issue.argtypes = [i32, i32, i32, vp, i32, vp]
@@ -205,7 +205,8 @@ def _best_ms(fn, n=10):
 
 def measure_peaks(P):
     """Ceilings of this device from hand-written probe kernels: an HBM streaming
-    read of 4 GiB, a gather of random 4 KiB slabs (decode's access shape), a
+    read of 4 GiB and a gather of random 4 KiB slabs (decode's access shape),
+    each with plain and with non-temporal loads, a
     gather of random 512-byte rows from a 2 MiB L2-resident buffer (the
     packed-query kernel's), dense MFMA loops at two waves per SIMD, and the
     instruction-issue and MFMA / VALU co-execution probes."""
@@ -221,20 +222,25 @@ def measure_peaks(P):
         if rc != 0:
             raise RuntimeError(f"{what} failed (HIP error {-rc})")
 
-    # each ceiling is the best over 4, 8, 16 and 32 waves per CU
-    best = 0.0
-    for mult in (1, 2, 4, 8):
-        ms = _best_ms(lambda: ok(L.pkb_peak_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(),
-                                                     ncu * mult, st), "hbm read"))
-        best = max(best, nbytes / (ms * 1e-3) / 1e9)
-    out["hbm_read_GBps"] = best
+    # each ceiling is the best over 4, 8, 16 and 32 waves per CU; the HBM ones
+    # also over plain and non-temporal loads (both are reported)
     got = ctypes.c_int64(0)
-    best = 0.0
-    for mult in (1, 2, 4, 8):
-        ms = _best_ms(lambda: ok(L.pkb_peak_hbm_gather(buf.data_ptr(), nbytes, 1 << 20, sink.data_ptr(),
-                                                       ncu * mult, ctypes.byref(got), st), "hbm gather"))
-        best = max(best, got.value / (ms * 1e-3) / 1e9)
-    out["hbm_gather_4k_GBps"] = best
+    for nt, tag in ((0, "plain"), (1, "nt")):
+        best = 0.0
+        for mult in (1, 2, 4, 8):
+            ms = _best_ms(lambda: ok(L.pkb_peak_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                                         ncu * mult, nt, st), "hbm read"))
+            best = max(best, nbytes / (ms * 1e-3) / 1e9)
+        out[f"hbm_read_{tag}_GBps"] = best
+        best = 0.0
+        for mult in (1, 2, 4, 8):
+            ms = _best_ms(lambda: ok(L.pkb_peak_hbm_gather(buf.data_ptr(), nbytes, 1 << 20, sink.data_ptr(),
+                                                           ncu * mult, nt, ctypes.byref(got), st),
+                                     "hbm gather"))
+            best = max(best, got.value / (ms * 1e-3) / 1e9)
+        out[f"hbm_gather_4k_{tag}_GBps"] = best
+    out["hbm_read_GBps"] = max(out["hbm_read_plain_GBps"], out["hbm_read_nt_GBps"])
+    out["hbm_gather_4k_GBps"] = max(out["hbm_gather_4k_plain_GBps"], out["hbm_gather_4k_nt_GBps"])
     small = 2 << 20
     best = 0.0
     for mult in (1, 2, 4, 8):

@@ -22,16 +22,20 @@ extern "C" {
 
 /* Streaming read of `bytes` (a multiple of 4096) from `buf`: every byte once;
  * consecutive waves read consecutive 4 KiB chunks, each wave keeping four
- * chunks (16 loads of 16 bytes per lane) in flight. */
-int pkb_peak_hbm_read(const void* buf, int64_t bytes, void* sink, int32_t grid, void* stream);
+ * chunks (16 loads of 16 bytes per lane) in flight.  `nontemporal` 1 marks
+ * the loads non-temporal (the nt cache policy), 0 leaves them plain; any other
+ * value is rejected. */
+int pkb_peak_hbm_read(const void* buf, int64_t bytes, void* sink, int32_t grid, int32_t nontemporal,
+                      void* stream);
 
 /* Gather of `n_reads` slabs of 4096 bytes at pseudo-random slab indices of
  * `buf` (`bytes` a multiple of 4096, at least one slab): the access shape of
  * paged decode (one 16-token page of one KV head at D = 128).  Each wave keeps
  * four slabs in flight; n_reads is rounded up to whole wave iterations
- * (returned bytes = 4096 * reads actually made, written to *bytes_read). */
+ * (returned bytes = 4096 * reads actually made, written to *bytes_read).
+ * `nontemporal` as for pkb_peak_hbm_read. */
 int pkb_peak_hbm_gather(const void* buf, int64_t bytes, int64_t n_reads, void* sink,
-                        int32_t grid, int64_t* bytes_read, void* stream);
+                        int32_t grid, int32_t nontemporal, int64_t* bytes_read, void* stream);
 
 /* Gather of 512-byte rows at pseudo-random row indices of a buffer small
  * enough to stay in each XCD's 4 MB L2 (`bytes` a multiple of 512, at most

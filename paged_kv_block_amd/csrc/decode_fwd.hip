@@ -142,7 +142,8 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, int b, int kv
   const char* vbase = (const char*)p.v;
   // Loads of one 32-key group.  K goes straight into the A operand of S^T;
   // V pieces are row-major (piece lane + 64i is key 4i + lane/16 at D = 128,
-  // 2i + lane/32 at D = 256, so each load's chunk is wave-uniform).
+  // 2i + lane/32 at D = 256, so each load's chunk is wave-uniform).  Every
+  // K/V byte is read once per launch, so the loads are non-temporal.
   auto load_group = [&](int64_t off_v, bf16x8 (&ka)[2][KS], u32x4 (&vr)[VP]) {
     if (RAGGED) {
       // row offset of key k of the group, held by lane k
@@ -155,14 +156,14 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, int b, int kv
       for (int u = 0; u < 2; ++u) {
         const int64_t off = row_off(16 * u + qn) * 2 + 16 * g;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) ka[u][s] = as_bf16x8(ld_global_16(kbase + off + 64 * s));
+        for (int s = 0; s < KS; ++s) ka[u][s] = as_bf16x8(ld_stream_16(kbase + off + 64 * s));
       }
 #pragma unroll
       for (int i = 0; i < VP; ++i) {
         const int piece = lane + 64 * i;
         const int key = piece / (D / 8);
         const int dp = piece - key * (D / 8);
-        vr[i] = ld_global_16(vbase + row_off(key) * 2 + dp * 16);
+        vr[i] = ld_stream_16(vbase + row_off(key) * 2 + dp * 16);
       }
       return;
     }
@@ -171,7 +172,7 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, int b, int kv
       const int64_t o0 = readlane_i64(off_v, 2 * u), o1 = readlane_i64(off_v, 2 * u + 1);
       const int64_t off = (qn < 8 ? o0 : o1) * 2 + ((qn & 7) * D + 8 * g) * 2;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) ka[u][s] = as_bf16x8(ld_global_16(kbase + off + 64 * s));
+      for (int s = 0; s < KS; ++s) ka[u][s] = as_bf16x8(ld_stream_16(kbase + off + 64 * s));
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
@@ -179,7 +180,7 @@ __device__ __forceinline__ void decode_part(const DecodeParams& p, int b, int kv
       const int key = piece / (D / 8);
       const int dp = piece - key * (D / 8);
       const int64_t off = readlane_i64(off_v, (64 * i) / (D / 8) / 8) * 2 + ((key & 7) * D + dp * 8) * 2;
-      vr[i] = ld_global_16(vbase + off);
+      vr[i] = ld_stream_16(vbase + off);
     }
   };
 

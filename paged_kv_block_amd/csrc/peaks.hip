@@ -1,5 +1,6 @@
 // peaks.hip -- on-device ceilings for the roofline denominators: HBM streaming
-// read, HBM gather of 4 KiB slabs (paged decode's access shape), L2-resident
+// read, HBM gather of 4 KiB slabs (paged decode's access shape), each with
+// plain or non-temporal loads, L2-resident
 // gather of 512-byte rows (the packed-query sparse kernel's), and dense MFMA
 // loops in bf16, int8 and fp8.  Measurement code only.
 #include <hip/hip_runtime.h>
@@ -33,8 +34,16 @@ __device__ __forceinline__ uint32_t mix(uint32_t a, uint32_t b, uint32_t c) {
 
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v[0] ^ v[1] ^ v[2] ^ v[3]; }
 
+// 16 bytes per lane, plain or non-temporal (the nt cache policy).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const unsigned char* p) {
+  if (NT) return pkb::ld_stream_16(p);
+  return *(const u32x4*)p;
+}
+
 // Streaming read: consecutive waves read consecutive 4 KiB chunks, each wave
 // four chunks (16 KiB) in flight per iteration; every byte is read once.
+template <bool NT>
 __global__ void __launch_bounds__(256) hbm_read_kernel(const unsigned char* __restrict__ buf,
                                                       int64_t n_chunks, uint32_t* sink) {
   const int lane = threadIdx.x & 63;
@@ -48,7 +57,7 @@ __global__ void __launch_bounds__(256) hbm_read_kernel(const unsigned char* __re
       const int64_t c = c0 + s * tw;
       const unsigned char* p = buf + (c < n_chunks ? c : c0) * 4096 + lane * 16;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[s][k] = *(const u32x4*)(p + k * 1024);
+      for (int k = 0; k < 4; ++k) v[s][k] = ld16<NT>(p + k * 1024);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -59,6 +68,7 @@ __global__ void __launch_bounds__(256) hbm_read_kernel(const unsigned char* __re
 }
 
 // Each wave reads 4 slabs of 4 KiB per iteration (4 KiB = 4 loads of 1 KiB).
+template <bool NT>
 __global__ void __launch_bounds__(256) hbm_gather_kernel(const unsigned char* __restrict__ buf,
                                                         uint32_t n_slabs, int iters, uint32_t* sink) {
   const int lane = threadIdx.x & 63;
@@ -71,7 +81,7 @@ __global__ void __launch_bounds__(256) hbm_gather_kernel(const unsigned char* __
       const uint32_t slab = mix(gw, (uint32_t)it, (uint32_t)s) % n_slabs;
       const unsigned char* p = buf + (size_t)slab * 4096 + lane * 16;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[s][k] = *(const u32x4*)(p + k * 1024);
+      for (int k = 0; k < 4; ++k) v[s][k] = ld16<NT>(p + k * 1024);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -270,25 +280,36 @@ hipError_t allow_probe_lds() {
 
 extern "C" {
 
-int pkb_peak_hbm_read(const void* buf, int64_t bytes, void* sink, int32_t grid, void* stream) {
-  if (!buf || !sink || bytes < 4096 || bytes % 4096 || grid < 1) return -(int)hipErrorInvalidValue;
-  hbm_read_kernel<<<grid, 256, 0, (hipStream_t)stream>>>((const unsigned char*)buf, bytes / 4096,
-                                                         (uint32_t*)sink);
+int pkb_peak_hbm_read(const void* buf, int64_t bytes, void* sink, int32_t grid, int32_t nontemporal,
+                      void* stream) {
+  if (!buf || !sink || bytes < 4096 || bytes % 4096 || grid < 1 || (nontemporal & ~1))
+    return -(int)hipErrorInvalidValue;
+  if (nontemporal)
+    hbm_read_kernel<true><<<grid, 256, 0, (hipStream_t)stream>>>((const unsigned char*)buf, bytes / 4096,
+                                                                 (uint32_t*)sink);
+  else
+    hbm_read_kernel<false><<<grid, 256, 0, (hipStream_t)stream>>>((const unsigned char*)buf, bytes / 4096,
+                                                                  (uint32_t*)sink);
   return status(hipGetLastError());
 }
 
 int pkb_peak_hbm_gather(const void* buf, int64_t bytes, int64_t n_reads, void* sink,
-                        int32_t grid, int64_t* bytes_read, void* stream) {
+                        int32_t grid, int32_t nontemporal, int64_t* bytes_read, void* stream) {
   if (!buf || !sink || !bytes_read || bytes < 4096 || bytes % 4096 || grid < 1 || n_reads < 1 ||
-      bytes / 4096 > 0xFFFFFFFFLL)
+      bytes / 4096 > 0xFFFFFFFFLL || (nontemporal & ~1))
     return -(int)hipErrorInvalidValue;
   const int64_t per_iter = (int64_t)grid * 4 * 4;   // slabs per iteration over the grid
   const int64_t iters = (n_reads + per_iter - 1) / per_iter;
   if (iters > 0x7fffffff) return -(int)hipErrorInvalidValue;
   *bytes_read = iters * per_iter * 4096;
-  hbm_gather_kernel<<<grid, 256, 0, (hipStream_t)stream>>>((const unsigned char*)buf,
-                                                           (uint32_t)(bytes / 4096), (int)iters,
-                                                           (uint32_t*)sink);
+  if (nontemporal)
+    hbm_gather_kernel<true><<<grid, 256, 0, (hipStream_t)stream>>>((const unsigned char*)buf,
+                                                                   (uint32_t)(bytes / 4096), (int)iters,
+                                                                   (uint32_t*)sink);
+  else
+    hbm_gather_kernel<false><<<grid, 256, 0, (hipStream_t)stream>>>((const unsigned char*)buf,
+                                                                    (uint32_t)(bytes / 4096), (int)iters,
+                                                                    (uint32_t*)sink);
   return status(hipGetLastError());
 }
 
