@@ -601,18 +601,9 @@ attn_fwd_kernel(const AttnParams p) {
     }
   };
 
-  // ---------------- prologue: first tiles in flight, then Q ----------------
-  constexpr int LA = Lay::LA;
-  TM tmr[LA + 1];   // tmr[k] = tile j + k
-#pragma unroll
-  for (int k = 0; k <= LA; ++k) {
-    tmr[k].M = 0;
-    if (k < n_tiles) {
-      tmr[k] = tile_meta(k);
-      if (tmr[k].M && k < LA) issue_tile(tmr[k], k);
-    }
-  }
-
+  // ---------------- prologue: Q, then the first tiles in flight ----------------
+  // (Q depends on no load, so it goes out while the tile descriptors are still
+  // arriving; the first tile's copies wait for them.)
   bf16x8 qf[NKS];
   {
     const uint16_t* qrow = p.q + ((int64_t)(tok_base + my_i) * p.Hq + my_hq) * D + 8 * hh;
@@ -621,6 +612,16 @@ attn_fwd_kernel(const AttnParams p) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (row_ok) x = ld_global_16(qrow + 16 * s);
       qf[s] = as_bf16x8(x);
+    }
+  }
+  constexpr int LA = Lay::LA;
+  TM tmr[LA + 1];   // tmr[k] = tile j + k
+#pragma unroll
+  for (int k = 0; k <= LA; ++k) {
+    tmr[k].M = 0;
+    if (k < n_tiles) {
+      tmr[k] = tile_meta(k);
+      if (tmr[k].M && k < LA) issue_tile(tmr[k], k);
     }
   }
   // Q and every copy issued so far complete here, so no load issued before the
@@ -911,15 +912,28 @@ attn_fwd_kernel(const AttnParams p) {
       }
   } else {
     uint16_t* o = (uint16_t*)p.out + orow * D;
+    // dims 32d + 16k .. +15 of a row are split over lanes l (hh = 0) and l + 32;
+    // one swap across the half-waves gives each lane 16 contiguous bytes
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * d + 8 * g4 + 4 * hh;
-        u32x2 w;
-        w[0] = cvt_pk_bf16(oacc[d][4 * g4] * inv, oacc[d][4 * g4 + 1] * inv);
-        w[1] = cvt_pk_bf16(oacc[d][4 * g4 + 2] * inv, oacc[d][4 * g4 + 3] * inv);
-        *(u32x2*)(o + d0) = w;
+      for (int k2 = 0; k2 < 2; ++k2) {
+        uint32_t x[2], y[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          x[e] = cvt_pk_bf16(oacc[d][8 * k2 + 2 * e] * inv, oacc[d][8 * k2 + 2 * e + 1] * inv);
+          y[e] = cvt_pk_bf16(oacc[d][8 * k2 + 4 + 2 * e] * inv, oacc[d][8 * k2 + 4 + 2 * e + 1] * inv);
+        }
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const auto r = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+          // lanes 0-31: own (g4 = 2k2) then partner's g4 = 2k2 data; lanes 32-63:
+          // partner's g4 = 2k2 + 1 data then own
+          if (hh == 0) { w[e] = x[e]; w[2 + e] = r[1]; }
+          else { w[e] = r[0]; w[2 + e] = y[e]; }
+        }
+        *(u32x4*)(o + 32 * d + 16 * k2 + 8 * hh) = w;
       }
   }
   if (p.lse && hh == 0)
