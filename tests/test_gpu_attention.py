@@ -1,7 +1,8 @@
 """GPU parity of the bf16 attention kernels against the fp64 oracle.
 
 Small cases span several 64-key tiles and query tiles with ragged tails; the
-named workloads run at full size and are checked on sampled rows.  Bars: bf16
+named workloads run at full size and are checked on every row (long-context
+prefill: sampled rows).  Bars: bf16
 out 2e-2, fp32 out 2e-3, LSE 2e-3 (absolute).
 """
 import sys
@@ -124,23 +125,20 @@ def test_bsa_all_blocks_equals_prefill():
     assert (lse - lse_p).abs().max().item() <= 1e-5
 
 
-def test_long_bsa_sampled():
-    """Full-size long-context block-sparse workload: every query token and head of
-    request 1 (all 128 BSR rows of all 8 KV heads), plus sampled tokens of the
-    other requests."""
+def test_long_bsa_full():
+    """Full-size long-context block-sparse workload (the launch the benchmark
+    times): every output row and LSE of all 4 requests against the oracle, one
+    request at a time."""
     case = W.long_bsa()
     _say("long_bsa: generated")
     out, lse = run_bsa(case)
-    rng = np.random.default_rng(7)
-    toks = [(int(b), int(i)) for b, i in zip(rng.choice([0, 2, 3], 48), rng.integers(0, 8192, 48))]
-    toks += [(0, 0), (2, 64), (3, 8191), (0, 959)]
-    toks += [(1, i) for i in range(8192)]
-    ref_o, ref_l = oracle_bsa(case, tokens=toks)
-    got_o = np.stack([f64(out[b, i]) for b, i in toks])
-    got_l = np.stack([f64(lse[b * 8192 + i]) for b, i in toks])
-    assert_close(got_o, ref_o, TOL_BF16, "out")
-    assert_close(got_l, ref_l, TOL_LSE, "lse")
     assert torch.isfinite(out.float()).all()
+    for b in range(4):
+        toks = [(b, i) for i in range(8192)]
+        ref_o, ref_l = oracle_bsa(case, tokens=toks)
+        _say("long_bsa: oracle request", b)
+        assert_close(f64(out[b]), ref_o, TOL_BF16, f"out (request {b})")
+        assert_close(f64(lse[b * 8192:(b + 1) * 8192]), ref_l, TOL_LSE, f"lse (request {b})")
 
 
 # ----------------------------------------------------------------------------- prefill
@@ -191,17 +189,14 @@ def test_prefill_growing_scores():
 
 
 @pytest.mark.parametrize("D,w", [(128, -1), (128, 1024), (256, -1)])
-def test_batch_prefill_sampled(D, w):
+def test_batch_prefill_full(D, w):
+    """Full-size batch prefill (the benchmark's shapes): every output row and LSE."""
     case = W.batch_prefill(3, D=D, window_left=w)
     _say("batch_prefill", D, w, int(case.qo_indptr[-1]))
     out, lse = run_prefill(case)
-    rng = np.random.default_rng(8)
-    T = int(case.qo_indptr[-1])
-    rows = sorted(set([int(x) for x in rng.integers(0, T, 64)] + [0, T - 1] +
-                      [int(x) for x in case.qo_indptr[1:-1]]))
-    ref_o, ref_l = oracle_prefill(case, rows=rows)
-    assert_close(f64(out[rows]), ref_o, TOL_BF16, "out")
-    assert_close(f64(lse[rows]), ref_l, TOL_LSE, "lse")
+    ref_o, ref_l = oracle_prefill(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
 
 
 @pytest.mark.parametrize("D,w", [(128, -1), (128, 4096), (256, -1)])
@@ -336,15 +331,14 @@ def test_decode_long_requests_many_splits(mask, w):
     assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
 
 
-def test_batch_decode_sampled():
+def test_batch_decode_full():
+    """The headline batch decode workload: every request's output and LSE."""
     case = W.batch_decode()
     _say("batch_decode: generated", int(case.seq_lens.sum()))
     out, lse, S = run_decode(case)
-    reqs = [0, 1, 17, 33, 63] + [int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens))]
-    ref_o, ref_l = oracle_decode(case, requests=reqs)
-    assert_close(f64(out[reqs]), ref_o, TOL_BF16, f"out (splits={S})")
-    assert_close(f64(lse[reqs]), ref_l, TOL_LSE, "lse")
-    assert torch.isfinite(out.float()).all()
+    ref_o, ref_l = oracle_decode(case)
+    assert_close(f64(out), ref_o, TOL_BF16, f"out (splits={S})")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
 
 
 # ----------------------------------------------------------------------------- multi-token decode

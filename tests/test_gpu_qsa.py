@@ -66,15 +66,13 @@ def test_qsa_sweep(i):
     assert torch.equal(out, out32.to(torch.bfloat16))
 
 
-def test_qsa_long_sampled():
+def test_qsa_long_full():
+    """Full-size packed-query workload (4 x 4096 tokens): every token's outputs
+    and LSE."""
     case = W.qsa_long()
     _say("qsa_long: generated", case.q.shape[0], "tokens")
     out, out32, lse = run_qsa(case)
-    T = case.q.shape[0]
-    rng = np.random.default_rng(11)
-    toks = sorted(set(int(x) for x in rng.integers(0, T, 24)) | {0, 4095, 4096, T - 1})
-    ref_o, ref_l = oracle(case, tokens=toks)
-    assert_close(f64(out32[toks]), ref_o[toks], TOL_F32, "out_fp32")
-    assert_close(f64(out[toks]), ref_o[toks], TOL_BF16, "out")
-    assert_close(f64(lse[:, toks]), ref_l[:, toks], TOL_LSE, "lse")
-    assert torch.isfinite(out32).all()
+    ref_o, ref_l = oracle(case)
+    assert_close(f64(out32), ref_o, TOL_F32, "out_fp32")
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
