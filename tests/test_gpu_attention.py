@@ -385,6 +385,17 @@ def test_decode_q_single_pass_sweep(i):
     assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
 
 
+def test_batch_decode_q_full():
+    """The multi-token decode workload the benchmark times (B=64, 4 query tokens
+    per request, causal): every output row and LSE."""
+    case = W.batch_decode_q()
+    _say("batch_decode_q: generated", int(case.seq_lens.sum()))
+    out, lse, S = run_decode_q(case)
+    ref_o, ref_l = oracle_decode_q(case)
+    assert_close(f64(out), ref_o, TOL_BF16, f"out (splits={S})")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+
+
 @pytest.mark.parametrize("i", range(len(DECODE_Q_SWEEP)))
 def test_decode_q_sweep(i):
     B, Hq, Hkv, D, sl, ps, sq, mask, w, ncu = DECODE_Q_SWEEP[i]
