@@ -24,7 +24,7 @@
 // each chunk is one contiguous [8, D] slab of the HND pool; other page sizes
 // (block-sparse and decode pools) copy each row from its own page.  Tiles go HBM -> LDS through
 // direct-to-LDS loads (global_load_lds_dwordx4: 1 KB per wave instruction, no
-// registers) into a K ring and a V ring, one or two tiles ahead of use, with
+// registers) into a K ring and a V ring, one tile ahead of use, with
 // one workgroup barrier per tile.  Each copy takes its chunk's pool address
 // from SGPRs plus a per-lane 32-bit offset fixed per instruction, so issuing a
 // tile's copies needs no vector ALU work.  Rows are stored unpadded with their 16-byte
@@ -73,10 +73,10 @@ struct AttnLayout {
   static constexpr int KT = kKvTile;             // keys per tile
   static constexpr int ROWB = D * 2;             // bytes per K / V row
   static constexpr int TILE_B = KT * ROWB;       // bytes of a K (or V) tile
-  // Tiles of copy lookahead: tile t is copied LA iterations before it is read,
-  // into ring slots (LA+1 per ring) whose previous tile every wave has finished.
-  // One tile ahead keeps two workgroups per CU at D = 128 (64 KB each).
-  static constexpr int LA = (D == 128 && NW == 8) ? 2 : 1;
+  // Tiles of copy lookahead: tile t is copied LA = 1 iteration before it is
+  // read, into the ring slot (of two per ring) whose previous tile every wave
+  // has finished.  That keeps two workgroups per CU at D = 128 (64 KB each).
+  static constexpr int LA = 1;
   static constexpr int NSK = LA + 1;
   static constexpr int NSV = LA + 1;
   static constexpr int V_BASE = NSK * TILE_B;
@@ -842,9 +842,7 @@ attn_fwd_kernel(const AttnParams p) {
   // ---------------- tile loop ----------------
   // Iteration j: S_j, masks, softmax and O += V_j P_j.
   for (int j = 0; j < n_tiles; ++j) {
-    // tile j landed in every wave's share; tiles j+1 .. j+LA-1 may still fly
-    if (LA == 2 && j + 1 < n_tiles && tmr[1].M && !ragged) wait_vmcnt<2 * IPW>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<0>();     // tile j landed in this wave's share ...
     __syncthreads();     // ... and is visible; every wave is done with tile j-1
     // copies into the slots of tile j-1: a whole tile's go out during S
     const bool run = wave_rows && tmr[0].M;
