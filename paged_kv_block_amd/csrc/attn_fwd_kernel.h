@@ -925,11 +925,13 @@ attn_fwd_kernel(const AttnParams p) {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
+          // The swap exchanges x of lanes 32-63 with y of lanes 0-31.  Afterwards
+          // lanes 0-31 hold their own g4 = 2k2 data then the partner's, and lanes
+          // 32-63 the partner's g4 = 2k2 + 1 data then their own: in every lane
+          // the two results are the row's 16 bytes in order, with no select.
           const auto r = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
-          // lanes 0-31: own (g4 = 2k2) then partner's g4 = 2k2 data; lanes 32-63:
-          // partner's g4 = 2k2 + 1 data then own
-          if (hh == 0) { w[e] = x[e]; w[2 + e] = r[1]; }
-          else { w[e] = r[0]; w[2 + e] = y[e]; }
+          w[e] = r[0];
+          w[2 + e] = r[1];
         }
         *(u32x4*)(o + 32 * d + 16 * k2 + 8 * hh) = w;
       }
