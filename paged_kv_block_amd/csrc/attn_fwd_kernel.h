@@ -152,6 +152,7 @@ __device__ __forceinline__ float select_lanes(uint64_t mask, float x, float y) {
 
 // Slack of the softmax reference max, in log2 units.
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kSlackPow = 256.0f;   // 2^kRescaleSlack
 
 // One KV tile, wave-uniform.  CPW = chunks this wave copies (8 / waves).
 template <int CPW>
@@ -761,14 +762,41 @@ attn_fwd_kernel(const AttnParams p) {
           if (chunk_t(4 * kb + (i >> 2)) + (i & 3) < myw4) acc[kb][i] = -INFINITY;
     }
   };
-  // Online softmax of one masked S^T tile: new reference, probabilities packed
-  // as bf16 (P^T operands; lo = P - bf16(P) for fp32 output), and their sum.
-  // The reference only moves when the row max passes it by more than
-  // kRescaleSlack (log2 units), so P <= 2^kRescaleSlack and the rescale of O is
-  // rare; O / l does not depend on the reference.
+  // Online softmax of one masked S^T tile: probabilities packed as bf16 (P^T
+  // operands; lo = P - bf16(P) for fp32 output) and their sum.  The reference
+  // only moves when the row max passes it by more than kRescaleSlack (log2
+  // units), so P <= 2^kRescaleSlack and the rescale of O is rare; O / l does
+  // not depend on the reference.
   float m_ref, m_use, psum;
   bf16x8 pb[4], pl[4];
-  auto softmax = [&](f32x16 (&acc)[2]) {
+  // probabilities of the tile against reference mu, and this lane's sum
+  auto probs = [&](f32x16 (&acc)[2], float mu) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 w, wl4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float e0 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t], sl2, -mu));
+        const float e1 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t + 1], sl2, -mu));
+        psum = (s == 0 && t == 0) ? e0 + e1 : psum + (e0 + e1);   // (no add of a zero start)
+        w[t] = cvt_pk_bf16(e0, e1);
+        if (F32)
+          wl4[t] = cvt_pk_bf16(e0 - __uint_as_float(w[t] << 16), e1 - __uint_as_float(w[t] & 0xFFFF0000u));
+      }
+      pb[s] = as_bf16x8(w);
+      if (F32) pl[s] = as_bf16x8(wl4);
+    }
+  };
+  // Returns true when every row kept its reference (nothing to rescale).
+  auto softmax = [&](f32x16 (&acc)[2]) -> bool {
+    // Against the current reference first: when no lane's probabilities sum
+    // past 2^kRescaleSlack, none of them passes it, the reference stays and
+    // the row max is not needed.  (A NaN sum, from a row without a reference,
+    // fails the test as well.)
+    if (!__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
+      probs(acc, m_run);
+      if (!__builtin_amdgcn_ballot_w64(!(psum <= kSlackPow))) return true;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -778,21 +806,8 @@ attn_fwd_kernel(const AttnParams p) {
     const float m_new = mx * sl2;
     m_ref = (m_new > m_run + kRescaleSlack) ? m_new : m_run;
     m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 w, wl4;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float e0 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t], sl2, -m_use));
-        const float e1 = fast_exp2(__builtin_fmaf(acc[s >> 1][8 * (s & 1) + 2 * t + 1], sl2, -m_use));
-        psum = (s == 0 && t == 0) ? e0 + e1 : psum + (e0 + e1);   // (no add of a zero start)
-        w[t] = cvt_pk_bf16(e0, e1);
-        if (F32)
-          wl4[t] = cvt_pk_bf16(e0 - __uint_as_float(w[t] << 16), e1 - __uint_as_float(w[t] & 0xFFFF0000u));
-      }
-      pb[s] = as_bf16x8(w);
-      if (F32) pl[s] = as_bf16x8(wl4);
-    }
+    probs(acc, m_use);
+    return false;
   };
   // move every row's softmax reference to m_ref
   auto rescale = [&]() {
@@ -858,8 +873,8 @@ attn_fwd_kernel(const AttnParams p) {
       else compute_s(j % Lay::NSK, sc, nullptr, 0);
       __builtin_amdgcn_s_setprio(0);
       mask_s(tmr[0], sc);
-      softmax(sc);
-      rescale();
+      if (softmax(sc)) l_run += psum;
+      else rescale();
       __builtin_amdgcn_s_setprio(1);
       compute_pv(j % Lay::NSV);
       __builtin_amdgcn_s_setprio(0);
