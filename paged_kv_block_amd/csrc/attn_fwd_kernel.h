@@ -787,15 +787,17 @@ attn_fwd_kernel(const AttnParams p) {
       if (F32) pl[s] = as_bf16x8(wl4);
     }
   };
-  // Returns true when every row kept its reference (nothing to rescale).
-  auto softmax = [&](f32x16 (&acc)[2]) -> bool {
+  auto softmax = [&](f32x16 (&acc)[2]) {
     // Against the current reference first: when no lane's probabilities sum
     // past 2^kRescaleSlack, none of them passes it, the reference stays and
     // the row max is not needed.  (A NaN sum, from a row without a reference,
     // fails the test as well.)
     if (!__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
       probs(acc, m_run);
-      if (!__builtin_amdgcn_ballot_w64(!(psum <= kSlackPow))) return true;
+      if (!__builtin_amdgcn_ballot_w64(!(psum <= kSlackPow))) {
+        m_ref = m_use = m_run;
+        return;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -807,7 +809,6 @@ attn_fwd_kernel(const AttnParams p) {
     m_ref = (m_new > m_run + kRescaleSlack) ? m_new : m_run;
     m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     probs(acc, m_use);
-    return false;
   };
   // move every row's softmax reference to m_ref
   auto rescale = [&]() {
@@ -873,8 +874,8 @@ attn_fwd_kernel(const AttnParams p) {
       else compute_s(j % Lay::NSK, sc, nullptr, 0);
       __builtin_amdgcn_s_setprio(0);
       mask_s(tmr[0], sc);
-      if (softmax(sc)) l_run += psum;
-      else rescale();
+      softmax(sc);
+      rescale();
       __builtin_amdgcn_s_setprio(1);
       compute_pv(j % Lay::NSV);
       __builtin_amdgcn_s_setprio(0);
