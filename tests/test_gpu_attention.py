@@ -188,6 +188,31 @@ def test_prefill_growing_scores():
     assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
 
 
+@pytest.mark.parametrize("D", [128, 256])
+def test_prefill_score_spikes(D):
+    """Keys of the first 64 tokens scaled by 3 (a high early reference) and a
+    random 5% of the later ones by 4 (scores far past it): within one launch
+    some waves keep their reference for a tile, others find a lane whose
+    probabilities would pass the rescale slack and take the row max."""
+    case = W.make_prefill(480 + D, 2, [128, 300], [700, 500], 8, 2, D, 16, mask="causal",
+                          extra_pages=2)
+    ps = case.k.shape[2]
+    k = case.k.float()
+    rng = np.random.default_rng(D)
+    for b, L in enumerate(case.seq_lens):
+        for t in range(int(L)):
+            f = 3.0 if t < 64 else (4.0 if rng.random() < 0.05 else 1.0)
+            k[int(case.block_tables[b, t // ps]), :, t % ps, :] *= f
+    case.k = k.to(torch.bfloat16)
+    _say("prefill score spikes", D)
+    out, lse = run_prefill(case)
+    ref_o, ref_l = oracle_prefill(case)
+    assert_close(f64(out), ref_o, TOL_BF16, "out")
+    assert_close(f64(lse), ref_l, TOL_LSE, "lse")
+    out32, _ = run_prefill(case, out_dtype=torch.float32, with_lse=False)
+    assert_close(f64(out32), ref_o, TOL_F32, "out fp32")
+
+
 @pytest.mark.parametrize("D,w", [(128, -1), (128, 1024), (256, -1)])
 def test_batch_prefill_full(D, w):
     """Full-size batch prefill (the benchmark's shapes): every output row and LSE."""
